@@ -1,0 +1,160 @@
+/*
+ * mak.h -- C ABI of libmak.so: greedy decoding of a llama-family decoder on
+ * one MI355X (gfx950) GPU.
+ *
+ * The operations are the ones the "model-as-a-kernel" page lists in its
+ * Usage and API sections: pack a model's weights into a device program, run
+ * one decode step returning live fp32 logits, consume a prompt in chunks of
+ * at most eight tokens, generate greedily, and decode several sequences as a
+ * batch.  The model is a stack of RMSNorm decoder blocks with rotary
+ * attention (GQA, optional per-head qk RMSNorm), a SwiGLU MLP, plain unscaled
+ * rope, an LM head and greedy argmax (API section, "Supported" paragraph).
+ * Sampling is greedy only ("Requirements and limits" section).
+ *
+ * Conventions shared by every entry point
+ *   - Weights are bf16 bit patterns (uint16_t) in the [out, in] row-major
+ *     layout of a linear layer.  Host arrays are read during mak_load only.
+ *   - Positions are 0-based; prompt token i sits at position i.
+ *   - "d_" pointers are device memory on the model's GPU; all work is queued
+ *     on the stream given to mak_load and every call returns after that
+ *     stream has finished the call's work, unless stated otherwise.
+ *   - Return value: MAK_OK (0) or a negative MAK_E* code.  A failing call
+ *     performs all validation before any device work, so it leaves the
+ *     model and its KV cache unchanged.  mak_last_error() describes the last
+ *     failure of the calling thread.
+ *   - A model is not thread-safe; calls on one model must be serialised.
+ *
+ * Arithmetic: bf16 storage, fp64 accumulation of every dot product and fp64
+ * evaluation of exp/sqrt, with bf16 rounding at the op boundaries of eager
+ * bf16 execution ("model-as-a-kernel", Method section: arithmetic reproduces
+ * eager bf16 semantics op for op, fixed reduction trees, no floating-point
+ * atomics, bitwise deterministic output).
+ */
+#ifndef MAK_H
+#define MAK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAK_OK 0
+#define MAK_EINVAL (-1)   /* null pointer, shape mismatch or unsupported shape      */
+#define MAK_ERANGE (-2)   /* token, position, slot, batch or length out of range    */
+#define MAK_ENOMEM (-3)   /* arena smaller than mak_plan's figure                   */
+#define MAK_EDEVICE (-4)  /* HIP runtime error (message kept for mak_last_error)     */
+
+#define MAK_MAX_BATCH 8     /* columns of one decode batch                          */
+#define MAK_PREFILL_CHUNK 8 /* prompts are consumed in chunks of at most 8 tokens    */
+
+/* Model shape.  head_dim even and <= 256; hidden, intermediate and
+ * n_q_heads*head_dim multiples of 8; n_q_heads a multiple of n_kv_heads;
+ * 1 <= max_batch <= MAK_MAX_BATCH; max_seq >= 1. */
+typedef struct {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+    float rms_eps, rope_theta;
+    int32_t tie_embeddings; /* 1: the LM head is the embedding matrix           */
+    int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before rope        */
+    int32_t max_seq;        /* positions per KV slot                             */
+    int32_t max_batch;      /* KV slots = sequences decodable at once            */
+} mak_config;
+
+/* One decoder layer's weights (host bf16 bits). q_norm/k_norm are [head_dim]
+ * and must be NULL unless cfg.qk_norm. */
+typedef struct {
+    const uint16_t *attn_norm; /* [hidden]                          */
+    const uint16_t *wq;        /* [n_q_heads*head_dim, hidden]      */
+    const uint16_t *wk;        /* [n_kv_heads*head_dim, hidden]     */
+    const uint16_t *wv;        /* [n_kv_heads*head_dim, hidden]     */
+    const uint16_t *wo;        /* [hidden, n_q_heads*head_dim]      */
+    const uint16_t *q_norm;    /* [head_dim] or NULL                */
+    const uint16_t *k_norm;    /* [head_dim] or NULL                */
+    const uint16_t *mlp_norm;  /* [hidden]                          */
+    const uint16_t *w_gate;    /* [intermediate, hidden]            */
+    const uint16_t *w_up;      /* [intermediate, hidden]            */
+    const uint16_t *w_down;    /* [hidden, intermediate]            */
+} mak_layer_weights;
+
+typedef struct {
+    const uint16_t *embed;            /* [vocab, hidden]                    */
+    const uint16_t *lm_head;          /* [vocab, hidden], NULL when tied     */
+    const uint16_t *final_norm;       /* [hidden]                           */
+    const mak_layer_weights *layers;  /* [n_layers]                         */
+} mak_weights;
+
+typedef struct mak_model mak_model; /* opaque */
+
+/* Device bytes mak_load needs for this shape: packed weights, rope tables,
+ * max_batch KV slots of max_seq positions, and scratch.  No device work. */
+int mak_plan(const mak_config *cfg, size_t *arena_bytes);
+
+/* Pack the weights into the caller's device arena and build the phase
+ * program ("model-as-a-kernel", Method section: model load packs the weights
+ * and compiles the architecture into a program).  d_arena must stay valid
+ * until mak_free; the model owns its contents.  hip_stream is a hipStream_t
+ * (NULL = the default stream).  Synchronises the stream before returning,
+ * so the host weight arrays may be freed afterwards. */
+int mak_load(const mak_config *cfg, const mak_weights *w, void *d_arena, size_t arena_bytes,
+             void *hip_stream, mak_model **out);
+
+/* Consume n prompt tokens of sequence `slot` at positions start_pos ..
+ * start_pos+n-1, in chunks of at most MAK_PREFILL_CHUNK ("model-as-a-kernel",
+ * Usage: chunked prompt consumption).  start_pos may not exceed the slot's
+ * cached length.  If d_logits is not NULL it receives the fp32 logits [vocab]
+ * of the last prompt token.  n >= 1. */
+int mak_prefill(mak_model *m, int32_t slot, const int32_t *ids, int32_t n, int32_t start_pos,
+                float *d_logits);
+
+/* One decode step ("model-as-a-kernel", API: decode_step returns live fp32
+ * logits [V]): token at position pos of `slot` (pos <= cached length; a
+ * smaller pos rewinds).  d_logits (may be NULL) receives fp32 logits
+ * [vocab]; next_token (host, may be NULL) receives the greedy argmax (lowest
+ * index among equal maxima). */
+int mak_decode_step(mak_model *m, int32_t slot, int32_t token, int32_t pos, float *d_logits,
+                    int32_t *next_token);
+
+/* Greedy generation ("model-as-a-kernel", Usage: generate): reset `slot`,
+ * prefill the n-token prompt from position 0, then emit exactly max_new tokens
+ * into out_tokens (host, [max_new]); the first is the argmax of the prefill
+ * logits and each later token is fed back on the device without a host
+ * round trip.  Requires n + max_new - 1 <= max_seq. */
+int mak_generate(mak_model *m, int32_t slot, const int32_t *prompt, int32_t n, int32_t max_new,
+                 int32_t *out_tokens);
+
+/* Batched greedy decode ("model-as-a-kernel", API: decode_batch(tokens,
+ * positions, steps)): B sequences (distinct slots) advance together for
+ * `steps` steps; step 0 consumes tokens[b] at positions[b], each later step
+ * consumes the previous step's argmax at the next position.  out_tokens
+ * (host, [steps][B]) receives every argmax; d_logits (may be NULL) receives
+ * the fp32 logits [B][vocab] of the last step.  Each sequence's results do
+ * not depend on the others in the batch. */
+int mak_decode_batch(mak_model *m, int32_t B, const int32_t *slots, const int32_t *tokens,
+                     const int32_t *positions, int32_t steps, int32_t *out_tokens,
+                     float *d_logits);
+
+/* Copy the cached K (after qk-norm and rope) and V of `layer`, `slot`,
+ * positions [pos0, pos0+n) into host arrays k_out and v_out, each
+ * [n_kv_heads][n][head_dim] bf16 bits ("model-as-a-kernel", Correctness
+ * section: the layer KV cache is compared bitwise against the reference).
+ * Requires pos0 + n <= the slot's cached length. */
+int mak_read_kv(const mak_model *m, int32_t layer, int32_t slot, int32_t pos0, int32_t n,
+                uint16_t *k_out, uint16_t *v_out);
+
+/* Number of sequences one batch may hold (the model's KV slots). */
+int mak_batch_max(const mak_model *m);
+
+/* Cached length (next free position) of a slot, or a negative error code. */
+int mak_slot_length(const mak_model *m, int32_t slot);
+
+/* Release the model's host-side state (the arena stays the caller's). */
+void mak_free(mak_model *m);
+
+/* Message of the calling thread's last failure ("" if none). */
+const char *mak_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAK_H */

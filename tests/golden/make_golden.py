@@ -1,0 +1,72 @@
+"""Write the oracle's reference outputs for the full-size workloads.
+
+Calls only ``oracle/`` (and the shared seeded input generator).  For each
+workload it runs greedy generation in the oracle and stores, per sequence:
+the prompt, the generated tokens, the oracle's top-2 logit gap at every
+step, and at a few sampled steps the fp32 logits at fixed sampled vocabulary
+indices plus the 16 largest logits.  The GPU tests replay the same token
+stream (teacher forcing) and compare against these values.
+
+usage: python tests/golden/make_golden.py [workload ...]
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from oracle import oracle as O                      # noqa: E402
+from transformer_forward_pass_amd import synth      # noqa: E402
+
+N_SAMPLE_IDX = 512
+
+
+def sample_steps(max_new):
+    return sorted({0, 1, 2, max_new // 2, max_new - 1})
+
+
+def sample_indices(vocab):
+    rng = np.random.default_rng(7)
+    return sorted(int(i) for i in rng.choice(vocab, size=min(N_SAMPLE_IDX, vocab), replace=False))
+
+
+def make(name):
+    wl = synth.WORKLOADS[name]
+    s = wl.shape
+    t0 = time.time()
+    w = synth.make_weights(s)
+    prompts = synth.make_prompts(wl)
+    idx = sample_indices(s.vocab)
+    steps = sample_steps(wl.max_new)
+    seqs = []
+    for b, p in enumerate(prompts):
+        o = O.Oracle(s, w, max_len=len(p) + wl.max_new)
+        toks, gaps, lgs = o.generate(p, wl.max_new, chunk=wl.chunk, keep_logits=True)
+        samples = {}
+        for st in steps:
+            lg = lgs[st]
+            top = np.argsort(-lg, kind="stable")[:16]
+            samples[str(st)] = {"idx_val": [float(lg[i]) for i in idx],
+                                "top_idx": [int(i) for i in top],
+                                "top_val": [float(lg[i]) for i in top]}
+        seqs.append({"prompt": [int(t) for t in p], "tokens": toks,
+                     "gaps": [float(g) for g in gaps], "samples": samples})
+        print("%s seq %d/%d done %.1fs" % (name, b + 1, len(prompts), time.time() - t0), flush=True)
+    out = {"source": "tests/golden/make_golden.py (oracle/ only)",
+           "workload": name, "weights_sha256": synth.weights_digest(w),
+           "max_new": wl.max_new, "chunk": wl.chunk, "sample_idx": idx,
+           "sample_steps": steps, "sequences": seqs}
+    path = os.path.join(HERE, name + ".json")
+    with open(path, "w") as f:
+        json.dump(out, f, separators=(",", ":"))
+    print("wrote", path, "%.1fs" % (time.time() - t0), flush=True)
+
+
+if __name__ == "__main__":
+    for n in (sys.argv[1:] or list(synth.WORKLOADS)):
+        make(n)

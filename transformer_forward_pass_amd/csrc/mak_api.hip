@@ -1,0 +1,726 @@
+// mak_api.hip -- host side of libmak.so: validation, weight packing, arena
+// layout, rope tables, and the sequencing of the decode program's phases.
+//
+// "model-as-a-kernel" (Method section): model load packs the weights and
+// compiles the architecture into a program of phases; every phase is run by
+// all resident workgroups; prompts are consumed in chunks of at most eight
+// tokens; the model owns its buffers for its lifetime ("Requirements and
+// limits" section).  Here each phase is one kernel launch on the model's
+// stream (stream order is the barrier between phases).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mak.h"
+#include "mak_internal.h"
+
+// kernels.hip
+hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st);
+hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st);
+hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st);
+hipError_t mak_set_lds_limit(int bytes);
+size_t mak_attn_lds(const AttnPhase& p);
+int mak_gemv_nc(int ncols);
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                        \
+    do {                                                                                     \
+        hipError_t e_ = (expr);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail(MAK_EDEVICE, "%s failed: %s", #expr, hipGetErrorString(e_));         \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxGemvBlocks = 1024;      // grid cap of a GEMV phase (waves loop over tiles)
+constexpr int kLdsBudget = 60 * 1024;     // dynamic LDS per workgroup we rely on (static LDS < 4 KiB)
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int ilog2(int v)
+{
+    int l = 0;
+    while ((1 << (l + 1)) <= v) l++;
+    return l;
+}
+
+int gcd(int a, int b)
+{
+    while (b) {
+        int t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// Geometry of a packed [n, k] matrix.  r = rows per lane group: the largest
+// of {4, 2, 1} that still leaves >= 2048 tiles (one per resident wave), and
+// even when the rows are interleaved gate/up pairs.
+PackGeom make_geom(int64_t n, int k, bool pairs)
+{
+    PackGeom g{};
+    g.n_rows = (int32_t)n;
+    g.k = k;
+    const int C = k / 8;
+    const int lr = gcd(C, 64);
+    g.lr_log2 = ilog2(lr);
+    const int G = 64 / lr;
+    int r = pairs ? 2 : 1;
+    for (int cand : {4, 2}) {
+        if ((n + (int64_t)G * cand - 1) / ((int64_t)G * cand) >= 2048) {
+            r = cand;
+            break;
+        }
+    }
+    g.r = r;
+    const int64_t rows_per_tile = (int64_t)G * r;
+    g.n_tiles = (int32_t)((n + rows_per_tile - 1) / rows_per_tile);
+    g.bytes = (int64_t)g.n_tiles * rows_per_tile * k * 2;
+    return g;
+}
+
+// Row source of a packed matrix: up to 3 stacked [rows_i, k] blocks, or
+// interleaved pairs (row 2i = a[i], row 2i+1 = b[i]).
+struct RowSrc {
+    const uint16_t* part[3];
+    int64_t rows[3];
+    bool interleave;
+    const uint16_t* row(int64_t n, int k) const
+    {
+        if (interleave) return (n & 1 ? part[1] : part[0]) + (n >> 1) * (int64_t)k;
+        for (int i = 0; i < 3; i++) {
+            if (n < rows[i]) return part[i] + n * (int64_t)k;
+            n -= rows[i];
+        }
+        return nullptr;
+    }
+};
+
+void pack(const PackGeom& g, const RowSrc& src, std::vector<uint16_t>& out)
+{
+    const int k = g.k, C = k / 8;
+    const int lr = 1 << g.lr_log2, G = 64 / lr, J = C / lr;
+    out.assign((size_t)(g.bytes / 2), 0);
+    const int64_t rows_per_tile = (int64_t)G * g.r;
+    for (int64_t n = 0; n < g.n_rows; n++) {
+        const uint16_t* s = src.row(n, k);
+        const int64_t tile = n / rows_per_tile;
+        const int rr = (int)(n - tile * rows_per_tile);
+        const int grp = rr / g.r, ri = rr % g.r;
+        for (int c = 0; c < C; c++) {
+            const int j = c / lr, sl = c % lr;
+            const int64_t slot = ((tile * J + j) * g.r + ri) * 64 + grp * lr + sl;
+            std::memcpy(&out[(size_t)slot * 8], s + (size_t)c * 8, 16);
+        }
+    }
+}
+
+struct LayerDev {
+    size_t attn_norm, mlp_norm, q_norm, k_norm;
+    size_t w_qkv, w_o, w_gu, w_down;
+    size_t k_cache, v_cache;
+};
+
+struct Layout {
+    PackGeom g_embed, g_lm, g_qkv, g_o, g_gu, g_down;
+    size_t ctl, out_tokens, x, qkv, o, m, logits, part_val, part_idx;
+    size_t cos_t, sin_t, embed, lm_head, final_norm;
+    std::vector<LayerDev> layers;
+    size_t total;
+    int qkv_ld;
+};
+
+int validate_cfg(const mak_config* c)
+{
+    if (!c) return fail(MAK_EINVAL, "cfg is NULL");
+    if (c->n_layers < 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 0 || c->max_seq <= 0 ||
+        c->max_batch <= 0)
+        return fail(MAK_EINVAL, "non-positive dimension in cfg");
+    if (c->hidden % 8 || c->intermediate % 8 || (c->n_q_heads * c->head_dim) % 8)
+        return fail(MAK_EINVAL, "hidden, intermediate and q_dim must be multiples of 8");
+    if (c->head_dim % 8 || c->head_dim > 256)
+        return fail(MAK_EINVAL, "head_dim must be a multiple of 8 and <= 256");
+    if (c->n_q_heads % c->n_kv_heads)
+        return fail(MAK_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
+    if (c->n_q_heads / c->n_kv_heads > 32)
+        return fail(MAK_EINVAL, "more than 32 query heads per kv head");
+    if (c->max_batch > MAK_MAX_BATCH) return fail(MAK_EINVAL, "max_batch > %d", MAK_MAX_BATCH);
+    if (c->hidden > 4096) return fail(MAK_EINVAL, "hidden > 4096 is not supported");
+    if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0f))
+        return fail(MAK_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
+    if (c->max_seq > (1 << 20)) return fail(MAK_EINVAL, "max_seq too large");
+    const size_t attn_lds = (size_t)(c->n_q_heads / c->n_kv_heads) * c->head_dim * 4 +
+                            (size_t)4 * MAK_MAX_COLS * c->head_dim +
+                            (size_t)(c->n_q_heads / c->n_kv_heads) * c->max_seq * 2;
+    if (attn_lds > (size_t)kLdsBudget)
+        return fail(MAK_EINVAL, "attention workspace (%zu B of LDS) exceeds %d B: lower max_seq",
+                    attn_lds, kLdsBudget);
+    return MAK_OK;
+}
+
+Layout make_layout(const mak_config* c)
+{
+    Layout L{};
+    const int H = c->hidden, d = c->head_dim, I = c->intermediate, V = c->vocab;
+    const int q_dim = c->n_q_heads * d, kv_dim = c->n_kv_heads * d;
+    L.g_embed = make_geom(V, H, false);
+    L.g_lm = L.g_embed;
+    L.g_qkv = make_geom(q_dim + 2 * kv_dim, H, false);
+    L.g_o = make_geom(H, q_dim, false);
+    L.g_gu = make_geom(2 * (int64_t)I, H, true);
+    L.g_down = make_geom(H, I, false);
+    L.qkv_ld = q_dim + 2 * kv_dim;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L.ctl = take(sizeof(Ctl));
+    L.out_tokens = take((size_t)c->max_seq * MAK_MAX_COLS * 4);
+    L.x = take((size_t)MAK_MAX_COLS * H * 2);
+    L.qkv = take((size_t)MAK_MAX_COLS * L.qkv_ld * 2);
+    L.o = take((size_t)MAK_MAX_COLS * q_dim * 2);
+    L.m = take((size_t)MAK_MAX_COLS * I * 2);
+    L.logits = take((size_t)MAK_MAX_COLS * V * 4);
+    L.part_val = take((size_t)kMaxGemvBlocks * MAK_MAX_COLS * 4);
+    L.part_idx = take((size_t)kMaxGemvBlocks * MAK_MAX_COLS * 4);
+    L.cos_t = take((size_t)c->max_seq * (d / 2) * 2);
+    L.sin_t = take((size_t)c->max_seq * (d / 2) * 2);
+    L.embed = take((size_t)L.g_embed.bytes);
+    L.lm_head = c->tie_embeddings ? L.embed : take((size_t)L.g_lm.bytes);
+    L.final_norm = take((size_t)H * 2);
+    const size_t cache_bytes = (size_t)c->max_batch * c->n_kv_heads * c->max_seq * d * 2;
+    L.layers.resize(c->n_layers);
+    for (int l = 0; l < c->n_layers; l++) {
+        LayerDev& ld = L.layers[l];
+        ld.attn_norm = take((size_t)H * 2);
+        ld.mlp_norm = take((size_t)H * 2);
+        ld.q_norm = c->qk_norm ? take((size_t)d * 2) : 0;
+        ld.k_norm = c->qk_norm ? take((size_t)d * 2) : 0;
+        ld.w_qkv = take((size_t)L.g_qkv.bytes);
+        ld.w_o = take((size_t)L.g_o.bytes);
+        ld.w_gu = take((size_t)L.g_gu.bytes);
+        ld.w_down = take((size_t)L.g_down.bytes);
+        ld.k_cache = take(cache_bytes);
+        ld.v_cache = take(cache_bytes);
+    }
+    L.total = off;
+    return L;
+}
+
+uint16_t host_bf16(float f)
+{
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace
+
+struct mak_model {
+    mak_config cfg;
+    Layout L;
+    char* arena;
+    size_t arena_bytes;
+    hipStream_t stream;
+    std::vector<int32_t> slot_len;   // cached positions per slot
+    int gemv_blocks_cap;
+    int max_cols_by_k[2];            // unused for now
+    template <class T>
+    T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
+};
+
+namespace {
+
+// Blocks of a GEMV phase: one wave per tile up to the cap.
+int gemv_blocks(const PackGeom& g)
+{
+    const int waves = MAK_BLOCK / 64;
+    int b = (g.n_tiles + waves - 1) / waves;
+    return std::max(1, std::min(b, kMaxGemvBlocks));
+}
+
+// Largest column group whose bf16 input rows fit the LDS budget.
+int max_cols_for_k(int k)
+{
+    int n = kLdsBudget / (k * 2);
+    if (n >= 8) return 8;
+    if (n >= 4) return 4;
+    if (n >= 2) return 2;
+    return 1;
+}
+
+int run_gemv(mak_model* m, GemvPhase p, int ncols, int col0)
+{
+    // split the columns into groups whose inputs fit in LDS
+    const int step = (p.epi == EPI_LOGITS) ? ncols : max_cols_for_k(p.geo.k);
+    if (p.epi == EPI_LOGITS && max_cols_for_k(p.geo.k) < ncols)
+        return fail(MAK_EINVAL, "LM head input too wide for %d columns", ncols);
+    for (int c0 = 0; c0 < ncols; c0 += step) {
+        GemvPhase q = p;
+        q.col0 = col0 + c0;
+        q.ncols = std::min(step, ncols - c0);
+        q.n_blocks = gemv_blocks(q.geo);
+        if (q.epi == EPI_LOGITS && q.col0 != col0)
+            return fail(MAK_EINVAL, "internal: LM head split");
+        // host-side shape checks of what the kernel assumes
+        if (q.geo.k % 8 || q.ncols < 1 || q.ncols > MAK_MAX_COLS || q.col0 + q.ncols > MAK_MAX_COLS ||
+            (size_t)mak_gemv_nc(q.ncols) * q.geo.k * 2 > (size_t)kLdsBudget ||
+            (q.epi == EPI_SWIGLU && (q.geo.r % 2)))
+            return fail(MAK_EINVAL, "internal: bad GEMV phase");
+        HIP_TRY(mak_launch_gemv(q, m->stream));
+    }
+    return MAK_OK;
+}
+
+// One step of the program for the columns currently in the control block:
+// ncols columns; LM head (with argmax feedback) for [lm_begin, lm_begin+lm_count).
+int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens)
+{
+    const mak_config& c = m->cfg;
+    const Layout& L = m->L;
+    const int H = c.hidden, d = c.head_dim, q_dim = c.n_q_heads * d;
+    Ctl* ctl = m->at<Ctl>(L.ctl);
+    uint16_t* x = m->at<uint16_t>(L.x);
+    uint16_t* qkv = m->at<uint16_t>(L.qkv);
+    uint16_t* o = m->at<uint16_t>(L.o);
+    uint16_t* mm = m->at<uint16_t>(L.m);
+
+    for (int l = 0; l < c.n_layers; l++) {
+        const LayerDev& ld = L.layers[l];
+        int rc;
+        // RMSNorm + QKV
+        GemvPhase p{};
+        p.w = m->at<void>(ld.w_qkv);
+        p.geo = L.g_qkv;
+        p.in_kind = (l == 0) ? IN_GATHER_NORM : IN_NORM;
+        p.epi = EPI_STORE;
+        p.in = x;
+        p.in_ld = H;
+        p.eps = c.rms_eps;
+        p.norm_w = m->at<uint16_t>(ld.attn_norm);
+        p.embed = m->at<void>(L.embed);
+        p.embed_geo = L.g_embed;
+        p.x_store = x;
+        p.x_ld = H;
+        p.out = qkv;
+        p.out_ld = L.qkv_ld;
+        p.ctl = ctl;
+        if ((rc = run_gemv(m, p, ncols, 0))) return rc;
+
+        // attention
+        AttnPhase a{};
+        a.qkv = qkv;
+        a.qkv_ld = L.qkv_ld;
+        a.kc = m->at<uint16_t>(ld.k_cache);
+        a.vc = m->at<uint16_t>(ld.v_cache);
+        a.cos_t = m->at<uint16_t>(L.cos_t);
+        a.sin_t = m->at<uint16_t>(L.sin_t);
+        a.q_norm = c.qk_norm ? m->at<uint16_t>(ld.q_norm) : nullptr;
+        a.k_norm = c.qk_norm ? m->at<uint16_t>(ld.k_norm) : nullptr;
+        a.o = o;
+        a.ctl = ctl;
+        a.ncols = ncols;
+        a.n_q_heads = c.n_q_heads;
+        a.n_kv_heads = c.n_kv_heads;
+        a.head_dim = d;
+        a.max_seq = c.max_seq;
+        a.eps = c.rms_eps;
+        a.scale = (float)(1.0 / std::sqrt((double)d));
+        if (mak_attn_lds(a) > (size_t)kLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
+        HIP_TRY(mak_launch_attn(a, m->stream));
+
+        // O + residual
+        GemvPhase po{};
+        po.w = m->at<void>(ld.w_o);
+        po.geo = L.g_o;
+        po.in_kind = IN_RAW;
+        po.epi = EPI_RESIDUAL;
+        po.in = o;
+        po.in_ld = q_dim;
+        po.out = x;
+        po.out_ld = H;
+        po.ctl = ctl;
+        if ((rc = run_gemv(m, po, ncols, 0))) return rc;
+
+        // RMSNorm + gate/up + SwiGLU
+        GemvPhase pg{};
+        pg.w = m->at<void>(ld.w_gu);
+        pg.geo = L.g_gu;
+        pg.in_kind = IN_NORM;
+        pg.epi = EPI_SWIGLU;
+        pg.in = x;
+        pg.in_ld = H;
+        pg.eps = c.rms_eps;
+        pg.norm_w = m->at<uint16_t>(ld.mlp_norm);
+        pg.out = mm;
+        pg.out_ld = c.intermediate;
+        pg.ctl = ctl;
+        if ((rc = run_gemv(m, pg, ncols, 0))) return rc;
+
+        // down + residual
+        GemvPhase pd{};
+        pd.w = m->at<void>(ld.w_down);
+        pd.geo = L.g_down;
+        pd.in_kind = IN_RAW;
+        pd.epi = EPI_RESIDUAL;
+        pd.in = mm;
+        pd.in_ld = c.intermediate;
+        pd.out = x;
+        pd.out_ld = H;
+        pd.ctl = ctl;
+        if ((rc = run_gemv(m, pd, ncols, 0))) return rc;
+    }
+    if (lm_count > 0) {
+        GemvPhase p{};
+        p.w = m->at<void>(L.lm_head);
+        p.geo = L.g_lm;
+        p.in_kind = (c.n_layers == 0) ? IN_GATHER_NORM : IN_NORM;
+        p.epi = EPI_LOGITS;
+        p.in = x;
+        p.in_ld = H;
+        p.eps = c.rms_eps;
+        p.norm_w = m->at<uint16_t>(L.final_norm);
+        p.embed = m->at<void>(L.embed);
+        p.embed_geo = L.g_embed;
+        p.x_store = x;
+        p.x_ld = H;
+        p.logits = m->at<float>(L.logits);
+        p.logits_ld = c.vocab;
+        p.part_val = m->at<float>(L.part_val);
+        p.part_idx = m->at<int32_t>(L.part_idx);
+        p.out_tokens = d_out_tokens;
+        p.ctl = ctl;
+        int rc = run_gemv(m, p, lm_count, lm_begin);
+        if (rc) return rc;
+    }
+    return MAK_OK;
+}
+
+int set_cols(mak_model* m, const ColState* cols, int ncols, int step)
+{
+    HIP_TRY(mak_launch_set_ctl(m->at<Ctl>(m->L.ctl), cols, ncols, step, m->stream));
+    return MAK_OK;
+}
+
+// Consume ids[0..n) of `slot` from start_pos; LM head on the last token when
+// want_lm.  Leaves the control block holding the next decode column.
+int prefill_chunks(mak_model* m, int slot, const int32_t* ids, int n, int start_pos, bool want_lm,
+                   int step0)
+{
+    for (int c0 = 0; c0 < n; c0 += MAK_PREFILL_CHUNK) {
+        const int T = std::min(MAK_PREFILL_CHUNK, n - c0);
+        ColState cols[MAK_MAX_COLS] = {};
+        for (int t = 0; t < T; t++) {
+            cols[t].token = ids[c0 + t];
+            cols[t].pos = start_pos + c0 + t;
+            cols[t].slot = slot;
+            cols[t].first_pos = start_pos + c0;
+            cols[t].first_col = 0;
+        }
+        int rc = set_cols(m, cols, T, step0);
+        if (rc) return rc;
+        const bool last = c0 + T >= n;
+        rc = run_step(m, T, T - 1, (last && want_lm) ? 1 : 0, m->at<int32_t>(m->L.out_tokens));
+        if (rc) return rc;
+    }
+    return MAK_OK;
+}
+
+int check_model(const mak_model* m)
+{
+    if (!m) return fail(MAK_EINVAL, "model is NULL");
+    return MAK_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* mak_last_error(void) { return g_err.c_str(); }
+
+int mak_plan(const mak_config* cfg, size_t* arena_bytes)
+{
+    int rc = validate_cfg(cfg);
+    if (rc) return rc;
+    if (!arena_bytes) return fail(MAK_EINVAL, "arena_bytes is NULL");
+    *arena_bytes = make_layout(cfg).total;
+    return MAK_OK;
+}
+
+int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t arena_bytes,
+             void* hip_stream, mak_model** out)
+{
+    int rc = validate_cfg(cfg);
+    if (rc) return rc;
+    if (!w || !out || !d_arena) return fail(MAK_EINVAL, "NULL weights, arena or out pointer");
+    if (reinterpret_cast<uintptr_t>(d_arena) % kAlign)
+        return fail(MAK_EINVAL, "arena must be %zu-byte aligned", kAlign);
+    const mak_config& c = *cfg;
+    if (!w->embed || !w->final_norm || (c.n_layers > 0 && !w->layers))
+        return fail(MAK_EINVAL, "missing embed, final_norm or layers");
+    if (!c.tie_embeddings && !w->lm_head) return fail(MAK_EINVAL, "untied model needs lm_head");
+    for (int l = 0; l < c.n_layers; l++) {
+        const mak_layer_weights& lw = w->layers[l];
+        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.mlp_norm || !lw.w_gate ||
+            !lw.w_up || !lw.w_down)
+            return fail(MAK_EINVAL, "layer %d: missing weight", l);
+        if (c.qk_norm ? (!lw.q_norm || !lw.k_norm) : (lw.q_norm || lw.k_norm))
+            return fail(MAK_EINVAL, "layer %d: q_norm/k_norm must be given iff qk_norm", l);
+    }
+    Layout L = make_layout(cfg);
+    if (arena_bytes < L.total)
+        return fail(MAK_ENOMEM, "arena has %zu bytes, needs %zu", arena_bytes, L.total);
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    HIP_TRY(mak_set_lds_limit(kLdsBudget));
+    char* A = reinterpret_cast<char*>(d_arena);
+    const int H = c.hidden, d = c.head_dim, I = c.intermediate;
+    const int q_dim = c.n_q_heads * d, kv_dim = c.n_kv_heads * d;
+
+    std::vector<uint16_t> buf;
+    auto put = [&](size_t off, const void* src, size_t bytes) -> int {
+        HIP_TRY(hipMemcpyAsync(A + off, src, bytes, hipMemcpyHostToDevice, st));
+        HIP_TRY(hipStreamSynchronize(st));
+        return MAK_OK;
+    };
+    auto put_packed = [&](size_t off, const PackGeom& g, const RowSrc& s) -> int {
+        pack(g, s, buf);
+        return put(off, buf.data(), buf.size() * 2);
+    };
+    HIP_TRY(hipMemsetAsync(A, 0, L.total, st));
+    if ((rc = put_packed(L.embed, L.g_embed, RowSrc{{w->embed, nullptr, nullptr}, {c.vocab, 0, 0}, false})))
+        return rc;
+    if (!c.tie_embeddings &&
+        (rc = put_packed(L.lm_head, L.g_lm, RowSrc{{w->lm_head, nullptr, nullptr}, {c.vocab, 0, 0}, false})))
+        return rc;
+    if ((rc = put(L.final_norm, w->final_norm, (size_t)H * 2))) return rc;
+    for (int l = 0; l < c.n_layers; l++) {
+        const mak_layer_weights& lw = w->layers[l];
+        const LayerDev& ld = L.layers[l];
+        if ((rc = put(ld.attn_norm, lw.attn_norm, (size_t)H * 2))) return rc;
+        if ((rc = put(ld.mlp_norm, lw.mlp_norm, (size_t)H * 2))) return rc;
+        if (c.qk_norm) {
+            if ((rc = put(ld.q_norm, lw.q_norm, (size_t)d * 2))) return rc;
+            if ((rc = put(ld.k_norm, lw.k_norm, (size_t)d * 2))) return rc;
+        }
+        if ((rc = put_packed(ld.w_qkv, L.g_qkv, RowSrc{{lw.wq, lw.wk, lw.wv}, {q_dim, kv_dim, kv_dim}, false})))
+            return rc;
+        if ((rc = put_packed(ld.w_o, L.g_o, RowSrc{{lw.wo, nullptr, nullptr}, {H, 0, 0}, false}))) return rc;
+        if ((rc = put_packed(ld.w_gu, L.g_gu, RowSrc{{lw.w_gate, lw.w_up, nullptr}, {I, I, 0}, true})))
+            return rc;
+        if ((rc = put_packed(ld.w_down, L.g_down, RowSrc{{lw.w_down, nullptr, nullptr}, {H, 0, 0}, false})))
+            return rc;
+    }
+    // rope tables: inv_i = fp32(theta^(-2i/d)), a = fp32(pos * inv_i), bf16(cos a), bf16(sin a)
+    {
+        const int half = d / 2;
+        std::vector<uint16_t> ct((size_t)c.max_seq * half), stb((size_t)c.max_seq * half);
+        for (int i = 0; i < half; i++) {
+            const float inv = (float)std::pow((double)c.rope_theta, -2.0 * i / (double)d);
+            for (int p = 0; p < c.max_seq; p++) {
+                const float a = (float)p * inv;
+                ct[(size_t)p * half + i] = host_bf16((float)std::cos((double)a));
+                stb[(size_t)p * half + i] = host_bf16((float)std::sin((double)a));
+            }
+        }
+        if ((rc = put(L.cos_t, ct.data(), ct.size() * 2))) return rc;
+        if ((rc = put(L.sin_t, stb.data(), stb.size() * 2))) return rc;
+    }
+    HIP_TRY(hipStreamSynchronize(st));
+
+    mak_model* m = new (std::nothrow) mak_model();
+    if (!m) return fail(MAK_ENOMEM, "host allocation failed");
+    m->cfg = c;
+    m->L = std::move(L);
+    m->arena = A;
+    m->arena_bytes = arena_bytes;
+    m->stream = st;
+    m->slot_len.assign(c.max_batch, 0);
+    *out = m;
+    g_err.clear();
+    return MAK_OK;
+}
+
+int mak_batch_max(const mak_model* m) { return m ? m->cfg.max_batch : MAK_EINVAL; }
+
+int mak_slot_length(const mak_model* m, int32_t slot)
+{
+    if (!m) return fail(MAK_EINVAL, "model is NULL");
+    if (slot < 0 || slot >= m->cfg.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slot);
+    return m->slot_len[slot];
+}
+
+int mak_read_kv(const mak_model* m, int32_t layer, int32_t slot, int32_t pos0, int32_t n,
+                uint16_t* k_out, uint16_t* v_out)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    if (!k_out || !v_out || n < 0) return fail(MAK_EINVAL, "NULL output or n < 0");
+    if (layer < 0 || layer >= c.n_layers) return fail(MAK_ERANGE, "layer %d out of range", layer);
+    if (slot < 0 || slot >= c.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slot);
+    if (pos0 < 0 || (int64_t)pos0 + n > m->slot_len[slot])
+        return fail(MAK_ERANGE, "positions beyond the cached length %d", m->slot_len[slot]);
+    const int d = c.head_dim;
+    const LayerDev& ld = m->L.layers[layer];
+    for (int g = 0; g < c.n_kv_heads; g++) {
+        const size_t src = (((size_t)slot * c.n_kv_heads + g) * c.max_seq + pos0) * d * 2;
+        const size_t dst = (size_t)g * n * d;
+        HIP_TRY(hipMemcpyAsync(k_out + dst, m->arena + ld.k_cache + src, (size_t)n * d * 2,
+                               hipMemcpyDeviceToHost, m->stream));
+        HIP_TRY(hipMemcpyAsync(v_out + dst, m->arena + ld.v_cache + src, (size_t)n * d * 2,
+                               hipMemcpyDeviceToHost, m->stream));
+    }
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    return MAK_OK;
+}
+
+void mak_free(mak_model* m) { delete m; }
+
+int mak_prefill(mak_model* m, int32_t slot, const int32_t* ids, int32_t n, int32_t start_pos,
+                float* d_logits)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    if (!ids || n < 1) return fail(MAK_EINVAL, "ids NULL or n < 1");
+    if (slot < 0 || slot >= c.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slot);
+    if (start_pos < 0 || start_pos > m->slot_len[slot])
+        return fail(MAK_ERANGE, "start_pos %d beyond cached length %d", start_pos, m->slot_len[slot]);
+    if ((int64_t)start_pos + n > c.max_seq)
+        return fail(MAK_ERANGE, "start_pos + n = %lld exceeds max_seq %d", (long long)start_pos + n, c.max_seq);
+    for (int i = 0; i < n; i++)
+        if (ids[i] < 0 || ids[i] >= c.vocab) return fail(MAK_ERANGE, "token %d out of range", ids[i]);
+    if ((rc = prefill_chunks(m, slot, ids, n, start_pos, d_logits != nullptr, 0))) return rc;
+    if (d_logits)
+        HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)c.vocab * 4,
+                               hipMemcpyDeviceToDevice, m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    m->slot_len[slot] = start_pos + n;
+    return MAK_OK;
+}
+
+int mak_decode_step(mak_model* m, int32_t slot, int32_t token, int32_t pos, float* d_logits,
+                    int32_t* next_token)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    if (slot < 0 || slot >= c.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slot);
+    if (token < 0 || token >= c.vocab) return fail(MAK_ERANGE, "token %d out of range", token);
+    if (pos < 0 || pos >= c.max_seq) return fail(MAK_ERANGE, "pos %d out of range", pos);
+    if (pos > m->slot_len[slot])
+        return fail(MAK_ERANGE, "pos %d beyond cached length %d", pos, m->slot_len[slot]);
+    ColState cs{};
+    cs.token = token;
+    cs.pos = pos;
+    cs.slot = slot;
+    cs.first_pos = pos;
+    cs.first_col = 0;
+    if ((rc = set_cols(m, &cs, 1, 0))) return rc;
+    if ((rc = run_step(m, 1, 0, 1, m->at<int32_t>(m->L.out_tokens)))) return rc;
+    if (d_logits)
+        HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)c.vocab * 4,
+                               hipMemcpyDeviceToDevice, m->stream));
+    if (next_token)
+        HIP_TRY(hipMemcpyAsync(next_token, m->at<int32_t>(m->L.out_tokens), 4, hipMemcpyDeviceToHost,
+                               m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    m->slot_len[slot] = pos + 1;
+    return MAK_OK;
+}
+
+int mak_generate(mak_model* m, int32_t slot, const int32_t* prompt, int32_t n, int32_t max_new,
+                 int32_t* out_tokens)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    if (!prompt || !out_tokens || n < 1 || max_new < 1)
+        return fail(MAK_EINVAL, "NULL prompt/out_tokens, n < 1 or max_new < 1");
+    if (slot < 0 || slot >= c.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slot);
+    if ((int64_t)n + max_new - 1 > c.max_seq)
+        return fail(MAK_ERANGE, "n + max_new - 1 exceeds max_seq %d", c.max_seq);
+    for (int i = 0; i < n; i++)
+        if (prompt[i] < 0 || prompt[i] >= c.vocab) return fail(MAK_ERANGE, "token %d out of range", prompt[i]);
+    m->slot_len[slot] = 0;
+    if ((rc = prefill_chunks(m, slot, prompt, n, 0, true, 0))) return rc;
+    int32_t* d_out = m->at<int32_t>(m->L.out_tokens);
+    for (int s = 1; s < max_new; s++)
+        if ((rc = run_step(m, 1, 0, 1, d_out))) return rc;
+    HIP_TRY(hipMemcpyAsync(out_tokens, d_out, (size_t)max_new * 4, hipMemcpyDeviceToHost, m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    m->slot_len[slot] = n + max_new - 1;
+    return MAK_OK;
+}
+
+int mak_decode_batch(mak_model* m, int32_t B, const int32_t* slots, const int32_t* tokens,
+                     const int32_t* positions, int32_t steps, int32_t* out_tokens, float* d_logits)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    if (!slots || !tokens || !positions || !out_tokens || steps < 1)
+        return fail(MAK_EINVAL, "NULL argument or steps < 1");
+    if (B < 1 || B > c.max_batch || B > MAK_MAX_COLS)
+        return fail(MAK_ERANGE, "batch %d out of range (max %d)", B, c.max_batch);
+    if (steps > c.max_seq) return fail(MAK_ERANGE, "steps > max_seq");
+    ColState cols[MAK_MAX_COLS] = {};
+    for (int b = 0; b < B; b++) {
+        if (slots[b] < 0 || slots[b] >= c.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slots[b]);
+        for (int b2 = 0; b2 < b; b2++)
+            if (slots[b2] == slots[b]) return fail(MAK_EINVAL, "slot %d repeated in batch", slots[b]);
+        if (tokens[b] < 0 || tokens[b] >= c.vocab) return fail(MAK_ERANGE, "token %d out of range", tokens[b]);
+        if (positions[b] < 0 || positions[b] > m->slot_len[slots[b]])
+            return fail(MAK_ERANGE, "position %d beyond cached length of slot %d", positions[b], slots[b]);
+        if ((int64_t)positions[b] + steps > c.max_seq)
+            return fail(MAK_ERANGE, "position + steps exceeds max_seq for slot %d", slots[b]);
+        cols[b].token = tokens[b];
+        cols[b].pos = positions[b];
+        cols[b].slot = slots[b];
+        cols[b].first_pos = positions[b];
+        cols[b].first_col = b;
+    }
+    if ((rc = set_cols(m, cols, B, 0))) return rc;
+    int32_t* d_out = m->at<int32_t>(m->L.out_tokens);
+    for (int s = 0; s < steps; s++)
+        if ((rc = run_step(m, B, 0, B, d_out))) return rc;
+    HIP_TRY(hipMemcpyAsync(out_tokens, d_out, (size_t)steps * B * 4, hipMemcpyDeviceToHost, m->stream));
+    if (d_logits)
+        HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)B * c.vocab * 4,
+                               hipMemcpyDeviceToDevice, m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    for (int b = 0; b < B; b++) m->slot_len[slots[b]] = positions[b] + steps;
+    return MAK_OK;
+}
+
+}  // extern "C"

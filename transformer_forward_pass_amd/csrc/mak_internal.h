@@ -1,0 +1,110 @@
+// mak_internal.h -- plain-old-data shared by the host runtime and the gfx950
+// kernels: the packed-GEMV geometry, the per-column decode state and the
+// phase descriptors of the device program.
+#pragma once
+#include <stdint.h>
+
+#define MAK_WAVE 64
+#define MAK_BLOCK 256               // threads per workgroup (4 waves)
+#define MAK_MAX_COLS 8              // columns (batch rows / prefill tokens) per step
+
+// ---------------------------------------------------------------------------
+// Packed weight geometry.
+//
+// A [N, K] bf16 matrix (K a multiple of 8) is cut into 16-byte chunks of 8
+// consecutive inputs, C = K/8 chunks per row.  `lr` = gcd(C, 64) lanes of a
+// wave share one row; a wave therefore covers g = 64/lr row groups, each of
+// `r` rows.  One wave's tile is g*r rows.  Inside a tile, the 16-byte slots
+// are stored in the order [j][ri][lane] with j = chunk iteration (C/lr of
+// them), ri = row within the group and lane = group*lr + s, where slot
+// (j, ri, lane) holds chunk j*lr + s of row tile*g*r + group*r + ri.
+// Every wave load is therefore 64 lanes x 16 B = 1 KiB contiguous.  Rows past
+// N are zero padding.
+// ---------------------------------------------------------------------------
+struct PackGeom {
+    int32_t n_rows;    // N
+    int32_t k;         // K
+    int32_t lr_log2;   // log2(lanes per row)
+    int32_t r;         // rows per lane group (1, 2 or 4)
+    int32_t n_tiles;   // ceil(N / (g*r))
+    int32_t pad_;
+    int64_t bytes;     // packed size in bytes (n_tiles * g * r * K * 2)
+};
+
+// State of one column (one token being processed) of a step.
+struct ColState {
+    int32_t token;      // input token id
+    int32_t pos;        // position of this token in its sequence
+    int32_t slot;       // KV slot of the sequence
+    int32_t first_pos;  // position of the first column of this sequence in the step
+    int32_t first_col;  // index of that column
+    int32_t pad_[3];
+};
+
+// Device control block (lives in the arena).
+struct Ctl {
+    ColState cols[MAK_MAX_COLS];
+    int32_t ncols;       // columns in the current step
+    int32_t lm_begin;    // first column whose logits are computed
+    int32_t lm_count;    // number of such columns
+    int32_t step;        // tokens emitted so far by the current call
+    uint32_t ticket;     // arrival counter of the LM-head argmax reduction
+    int32_t err;         // device-side error flag
+    int32_t pad_[2];
+};
+
+enum InKind : int32_t {
+    IN_RAW = 0,          // bf16 vectors in[col*in_ld + k]
+    IN_NORM = 1,         // RMSNorm(x[col]) with norm_w
+    IN_GATHER_NORM = 2,  // RMSNorm(embedding row of cols[col].token); block 0 also stores x
+};
+
+enum EpiKind : int32_t {
+    EPI_STORE = 0,       // out[col*out_ld + row] = bf16(acc)
+    EPI_RESIDUAL = 1,    // x[col*out_ld + row] = bf16(x + bf16(acc))
+    EPI_SWIGLU = 2,      // rows (2i, 2i+1) = (gate_i, up_i) -> out[col*out_ld + i]
+    EPI_LOGITS = 3,      // logits[col*logits_ld + row] = fp32(acc); argmax + feedback
+};
+
+struct GemvPhase {
+    const void* w;            // packed weights (PackGeom layout)
+    PackGeom geo;
+    int32_t in_kind;
+    int32_t epi;
+    int32_t ncols;            // active columns
+    int32_t col0;             // first column (of Ctl.cols) this phase works on
+    const uint16_t* in;       // IN_RAW / IN_NORM source, [col][in_ld]
+    int32_t in_ld;
+    float eps;
+    const uint16_t* norm_w;   // [K] for IN_NORM / IN_GATHER_NORM
+    const void* embed;        // packed embedding (IN_GATHER_NORM)
+    PackGeom embed_geo;
+    uint16_t* x_store;        // IN_GATHER_NORM: block 0 writes gathered rows here
+    int32_t x_ld;
+    int32_t out_ld;
+    uint16_t* out;            // EPI_STORE / EPI_RESIDUAL / EPI_SWIGLU destination
+    float* logits;            // EPI_LOGITS destination [col][logits_ld]
+    int32_t logits_ld;
+    int32_t n_blocks;         // grid size (EPI_LOGITS ticket count)
+    float* part_val;          // EPI_LOGITS per-block partial maxima [n_blocks][MAK_MAX_COLS]
+    int32_t* part_idx;
+    int32_t* out_tokens;      // EPI_LOGITS: emitted tokens [step][lm_count] (device)
+    Ctl* ctl;
+};
+
+struct AttnPhase {
+    const uint16_t* qkv;      // raw projections [col][qkv_ld]: q | k | v
+    int32_t qkv_ld;
+    uint16_t* kc;             // this layer's K cache  [slot][Hkv][max_seq][d]
+    uint16_t* vc;             // this layer's V cache
+    const uint16_t* cos_t;    // rope tables [max_seq][d/2] (bf16)
+    const uint16_t* sin_t;
+    const uint16_t* q_norm;   // [d] or null
+    const uint16_t* k_norm;
+    uint16_t* o;              // attention output [col][Hq*d]
+    Ctl* ctl;
+    int32_t ncols;
+    int32_t n_q_heads, n_kv_heads, head_dim, max_seq;
+    float eps;
+    float scale;              // fp32(1/sqrt(head_dim))
+};
