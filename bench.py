@@ -1,0 +1,186 @@
+"""Greedy-decode benchmark on one MI355X.
+
+One step = one mak_generate call of the SmolLM2-135M-shaped random-init model:
+a 32-token prompt consumed in chunks of 8, then 128 greedy tokens at batch 1
+with on-device token feedback -- every phase of the decode path (embedding
+gather, RMSNorm, Q/K/V/O and SwiGLU GEMVs, rope, GQA attention over the KV
+cache, LM head, argmax).  value = generated tokens per second over the K
+timed steps (the "model-as-a-kernel" page's measurement: 128 greedy tokens
+after a 32-token prompt, section "Measured").
+
+Also printed, in the same JSON line:
+  roofline      -- the dominant kernel (the phase kind with the largest total
+                   time) measured with HIP events on the model's stream over
+                   a second pass of the same K steps: algorithmic bytes per
+                   launch / average launch duration, against 8 TB/s.
+  cpu_baseline  -- the CPU oracle on a bounded sample of the same workload.
+  token_roofline -- bytes one decode token must stream (weights + KV) per
+                   steady-state decode token time, against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "smollm2-135m"
+SECONDARY = "llama-3.2-1b"
+
+
+def _gemv_bytes(shape, kind):
+    """Algorithmic bytes of one launch of a phase kind at batch 1: weight
+    bytes streamed once + activation vectors read and written (bf16)."""
+    H, I, d = shape.hidden, shape.intermediate, shape.head_dim
+    qd, kvd = shape.q_dim, shape.kv_dim
+    if kind == "qkv":
+        return 2 * (qd + 2 * kvd) * H + 2 * (H + H) + 2 * (qd + 2 * kvd)
+    if kind == "o":
+        return 2 * H * qd + 2 * qd + 2 * 2 * H
+    if kind == "gateup":
+        return 2 * 2 * I * H + 2 * (H + H) + 2 * I
+    if kind == "down":
+        return 2 * H * I + 2 * I + 2 * 2 * H
+    if kind == "lmhead":
+        return 2 * shape.vocab * H + 2 * (H + H) + 4 * shape.vocab
+    return None
+
+
+def run_gpu(args, shape, wl, w, prompt, steps):
+    import torch
+    from transformer_forward_pass_amd import mak
+    m = mak.MakModel(shape, w, device="cuda:0", max_seq=shape.max_seq)
+    max_new = wl.max_new
+    for _ in range(args.warmup):
+        m.generate(prompt, max_new)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m.generate(prompt, max_new)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    # the prompt alone (chunked prefill + LM head), timed the same way, to
+    # separate the steady-state decode rate
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        m.prefill(prompt, want_logits=True)
+    torch.cuda.synchronize()
+    t_prefill = (time.perf_counter() - t1) / steps
+
+    # second pass with per-launch HIP events on the model's stream
+    m.set_phase_timing(True)
+    for _ in range(steps):
+        m.generate(prompt, max_new)
+    times = m.phase_times()
+    m.set_phase_timing(False)
+    m.free()
+    return dt, t_prefill, times
+
+
+def measure(args, name, steps):
+    """Throughput, token roofline and dominant-kernel roofline of one workload."""
+    from transformer_forward_pass_amd import synth
+    wl = synth.WORKLOADS[name]
+    shape = wl.shape
+    w = synth.make_weights(shape)
+    prompt = synth.make_prompts(wl)[0]
+    dt, t_prefill, times = run_gpu(args, shape, wl, w, prompt, steps)
+    p0, n = len(prompt), wl.max_new
+    t_decode = (dt / steps - t_prefill) / (n - 1)
+    kinds = [k for k in ("qkv", "o", "gateup", "down", "lmhead") if times[k][1]]
+    dom = max(kinds, key=lambda k: times[k][0])
+    avg_s = times[dom][0] / times[dom][1] / 1e3
+    per_launch = _gemv_bytes(shape, dom)
+    achieved = per_launch / avg_s / 1e9
+    avg_pos = p0 + (n - 2) / 2.0
+    tok_bytes = shape.streamed_weight_bytes() + shape.kv_bytes_per_position() * (avg_pos + 1)
+    tok_gbs = tok_bytes / t_decode / 1e9
+    return {
+        "shape": shape, "w": w, "prompt": prompt, "wl": wl,
+        "tok_s": n * steps / dt, "ms_per_step": 1e3 * dt / steps,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": per_launch,
+                     "avg_launch_us": round(avg_s * 1e6, 3), "launches": times[dom][1]},
+        "token_roofline": {"decode_tok_s": round(1.0 / t_decode, 2), "bytes_per_token": int(tok_bytes),
+                           "achieved_gbs": round(tok_gbs, 2), "frac": round(tok_gbs / HBM_PEAK_GBS, 4),
+                           "prefill_ms": round(t_prefill * 1e3, 4)},
+        "phase_ms_per_step": {k: round(v[0] / steps, 4) for k, v in times.items()},
+    }
+
+
+def cpu_baseline(shape, w, prompt, n_new):
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    o = O.Oracle(shape, w, max_len=len(prompt) + n_new + 1)
+    t0 = time.perf_counter()
+    o.generate(prompt, n_new)
+    dt = time.perf_counter() - t0
+    return {"value": n_new / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": "the same model, %d-token prompt, %d greedy tokens (%.1f s)" % (
+                len(prompt), n_new, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-new", type=int, default=24, help="greedy tokens of the CPU sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 1B-shape measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    from transformer_forward_pass_amd import mak
+    if not os.path.exists(mak.LIB_PATH):
+        from transformer_forward_pass_amd import build as B
+        B.build()
+    r = measure(args, WORKLOAD, args.steps)
+    wl = r["wl"]
+    p0, n = len(r["prompt"]), wl.max_new
+    out = {
+        "metric": "greedy decode tok/s at batch 1 (135M/1B shapes); % of HBM weight-streaming roofline",
+        "value": round(r["tok_s"], 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of 8) + "
+                               "%d greedy tokens, batch 1" % (WORKLOAD, p0, n),
+                   "accumulate": "f64"},
+        "roofline": r["roofline"],
+        "token_roofline": r["token_roofline"],
+        "phase_ms_per_step": r["phase_ms_per_step"],
+    }
+    if not args.no_secondary:
+        r2 = measure(args, SECONDARY, max(2, args.steps // 2))
+        out["secondary"] = {"workload": "%s-shaped random-init decoder: 32-token prompt + 128 greedy "
+                                        "tokens, batch 1" % SECONDARY,
+                            "value": round(r2["tok_s"], 2), "unit": "tok/s",
+                            "ms_per_step": round(r2["ms_per_step"], 4),
+                            "roofline": r2["roofline"], "token_roofline": r2["token_roofline"],
+                            "phase_ms_per_step": r2["phase_ms_per_step"]}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(r["shape"], r["w"], r["prompt"], args.cpu_new)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

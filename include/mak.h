@@ -142,6 +142,32 @@ int mak_decode_batch(mak_model *m, int32_t B, const int32_t *slots, const int32_
 int mak_read_kv(const mak_model *m, int32_t layer, int32_t slot, int32_t pos0, int32_t n,
                 uint16_t *k_out, uint16_t *v_out);
 
+/* Executor.  MAK_EXEC_GRAPH (the default) replays one captured hipGraph of
+ * the step's phase launches per step shape; MAK_EXEC_PHASED launches every
+ * phase as its own kernel from the host -- the page's phase-per-launch mode
+ * ("model-as-a-kernel", API: decode_step(..., phased=True); Method: bitwise
+ * identical to the fused mode). */
+#define MAK_EXEC_GRAPH 0
+#define MAK_EXEC_PHASED 1
+int mak_set_executor(mak_model *m, int executor);
+
+/* Per-phase timing ("model-as-a-kernel", API: decode_step_timed runs the
+ * phases one launch each and reports per-phase milliseconds).  While
+ * enabled, every kernel the model launches is bracketed by hipEvents on the
+ * model's stream and its duration is added to the total of its phase kind.
+ * Enabling resets the totals.  mak_phase_times fills ms[MAK_PHASE_COUNT] and
+ * launches[MAK_PHASE_COUNT] (either may be NULL). */
+#define MAK_PHASE_QKV 0    /* RMSNorm + Q/K/V GEMV                          */
+#define MAK_PHASE_ATTN 1   /* qk-norm, rope, KV append, attention           */
+#define MAK_PHASE_O 2      /* O GEMV + residual                             */
+#define MAK_PHASE_GATEUP 3 /* RMSNorm + gate/up GEMV + SwiGLU               */
+#define MAK_PHASE_DOWN 4   /* down GEMV + residual                          */
+#define MAK_PHASE_LMHEAD 5 /* final RMSNorm + LM head + argmax + feedback   */
+#define MAK_PHASE_CTL 6    /* control-block updates                         */
+#define MAK_PHASE_COUNT 7
+int mak_set_phase_timing(mak_model *m, int enable);
+int mak_phase_times(const mak_model *m, double *ms, int64_t *launches);
+
 /* Number of sequences one batch may hold (the model's KV slots). */
 int mak_batch_max(const mak_model *m);
 

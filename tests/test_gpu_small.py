@@ -170,3 +170,30 @@ def test_rewind_and_error_paths_leave_state_unchanged(torch_cuda):
     # rewinding to position 9 and re-feeding the last prompt token reproduces the logits
     again = _np(m.decode_step(p[-1], 9)[0])
     assert np.array_equal(again, base)
+
+
+def test_graph_replays_equal_phase_per_launch_bitwise(torch_cuda):
+    """The captured-graph executor equals the phase-per-launch executor
+    bitwise ("model-as-a-kernel", Method: the phase-per-launch debug mode is
+    bitwise identical to the fused mode), on every one of several replays
+    with unrelated eager GPU work and synchronisations in between."""
+    from transformer_forward_pass_amd import mak
+    s = dataclasses.replace(TINY, max_batch=2)
+    _, m = _model(s, max_batch=2)
+    p = _ids(s, 13)
+    m.set_executor(mak.EXEC_PHASED)
+    ref_tok = m.generate(p, 12)
+    ref_pre = _np(m.prefill(p))
+    m.prefill(p[:7], slot=1, want_logits=False)
+    ref_bt, ref_bl = m.decode_batch([5, 6], [13, 7], slots=[0, 1], steps=3)
+    ref_bl = _np(ref_bl)
+    m.set_executor(mak.EXEC_GRAPH)
+    junk = torch_cuda.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        assert m.generate(p, 12) == ref_tok, "replay %d" % rep
+        junk = (junk * 1.0001).sin()                 # unrelated eager work
+        torch_cuda.cuda.synchronize()
+        assert np.array_equal(_np(m.prefill(p)), ref_pre), "replay %d" % rep
+        m.prefill(p[:7], slot=1, want_logits=False)
+        bt, bl = m.decode_batch([5, 6], [13, 7], slots=[0, 1], steps=3)
+        assert np.array_equal(bt, ref_bt) and np.array_equal(_np(bl), ref_bl), "replay %d" % rep

@@ -31,20 +31,92 @@ __device__ __forceinline__ uint16_t f2bf(float f)
 // value of f rounded to bf16
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
-// fp64 sum over the 64 lanes of a wave; every lane gets the result.
-__device__ __forceinline__ double wave_sum(double v)
+// ---------------------------------------------------------------------------
+// Cross-lane moves.  DPP lane moves are VALU instructions (a few cycles)
+// where __shfl_xor goes through the LDS crossbar (ds_bpermute, ~100 cycles),
+// so reductions use DPP inside a 16-lane row and the crossbar only between
+// rows.  64-bit values move as two 32-bit halves.
+// ---------------------------------------------------------------------------
+enum : int {
+    DPP_XOR1 = 0xB1,        // quad_perm [1,0,3,2]
+    DPP_XOR2 = 0x4E,        // quad_perm [2,3,0,1]
+    DPP_HALF_MIRROR = 0x141,// lane i <-> 7-i within each 8 lanes
+    DPP_MIRROR = 0x140,     // lane i <-> 15-i within each row of 16
+    DPP_ROR4 = 0x124,       // rotate right by 4 within a row
+    DPP_ROR8 = 0x128,       // rotate right by 8 within a row
+};
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of 2^LOG lanes (LOG <= 6); every lane of a group
+// gets the group's sum (the same tree in every group).
+template <int LOG>
+__device__ __forceinline__ double group_sum(double v)
+{
+    if (LOG >= 1) v += dpp_d<DPP_XOR1>(v);
+    if (LOG >= 2) v += dpp_d<DPP_XOR2>(v);
+    if (LOG >= 3) v += dpp_d<DPP_HALF_MIRROR>(v);
+    if (LOG >= 4) v += dpp_d<DPP_MIRROR>(v);
+    if (LOG >= 5) v += __shfl_xor(v, 16, 64);
+    if (LOG >= 6) v += __shfl_xor(v, 32, 64);
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v)
+// Runtime group size (1 << log), log <= 6.
+__device__ __forceinline__ double group_sum_rt(double v, int log)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if (log >= 1) v += dpp_d<DPP_XOR1>(v);
+    if (log >= 2) v += dpp_d<DPP_XOR2>(v);
+    if (log >= 3) v += dpp_d<DPP_HALF_MIRROR>(v);
+    if (log >= 4) v += dpp_d<DPP_MIRROR>(v);
+    if (log >= 5) v += __shfl_xor(v, 16, 64);
+    if (log >= 6) v += __shfl_xor(v, 32, 64);
     return v;
 }
+
+template <int LOG>
+__device__ __forceinline__ float group_max(float v)
+{
+    if (LOG >= 1) v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    if (LOG >= 2) v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    if (LOG >= 3) v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    if (LOG >= 4) v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+    if (LOG >= 5) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if (LOG >= 6) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// Sum over lanes with equal (lane mod 2^LOG): the "stride" reduction that
+// folds lane groups of 2^LOG lanes onto each other.  Lanes of one residue
+// may differ in the last bit (association order); read one fixed lane.
+template <int LOG>
+__device__ __forceinline__ double stride_sum(double v)
+{
+    static_assert(LOG >= 1 && LOG <= 5, "stride 2..32");
+    if (LOG <= 1) v += dpp_d<0x122>(v);   // row_ror:2
+    if (LOG <= 2) v += dpp_d<DPP_ROR4>(v);
+    if (LOG <= 3) v += dpp_d<DPP_ROR8>(v);
+    if (LOG <= 4) v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// fp64 sum over the 64 lanes of a wave; every lane gets the result.
+__device__ __forceinline__ double wave_sum(double v) { return group_sum<6>(v); }
+
+__device__ __forceinline__ float wave_max(float v) { return group_max<6>(v); }
 
 // Block-wide fp64 sum (MAK_BLOCK threads); `red` holds >= 4 doubles of LDS.
 // Waves are combined in wave order, so the tree is fixed.

@@ -58,35 +58,37 @@ __device__ void stage_input(const GemvPhase& p, uint16_t* hs, double* red)
             for (int q = tid; q < (K >> 3); q += MAK_BLOCK) h4[q] = src[q];
             continue;
         }
-        // RMSNorm of x (from the residual stream, or an embedding row)
-        double ss = 0.0;
+        // RMSNorm of x (the residual stream, or an embedding row): x and the
+        // norm weight are loaded together and kept in registers (K <= 4096,
+        // so at most 2 chunks per thread)
+        const uint4* wn = reinterpret_cast<const uint4*>(p.norm_w);
+        uint4 xv[2], wv[2];
+        const uint4* src;
         if (p.in_kind == IN_NORM) {
-            const uint4* src = reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
-            for (int q = tid; q < (K >> 3); q += MAK_BLOCK) {
-                uint4 v = src[q];
-                h4[q] = v;
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    double a = bf_lo(u[e]), b = bf_hi(u[e]);
-                    ss = fma(a, a, ss);
-                    ss = fma(b, b, ss);
-                }
-            }
+            src = reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
         } else {  // IN_GATHER_NORM
-            const int tok = p.ctl->cols[col].token;
-            const uint4* E = reinterpret_cast<const uint4*>(p.embed);
-            uint4* xs = (blockIdx.x == 0)
-                            ? reinterpret_cast<uint4*>(p.x_store + (size_t)col * p.x_ld)
-                            : nullptr;
-            for (int q = tid; q < (K >> 3); q += MAK_BLOCK) {
-                uint4 v = E[packed_chunk(p.embed_geo, tok, q)];
-                h4[q] = v;
-                if (xs) xs[q] = v;
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+            src = reinterpret_cast<const uint4*>(p.embed);
+        }
+        const int tok = (p.in_kind == IN_GATHER_NORM) ? p.ctl->cols[col].token : 0;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int q = tid + i * MAK_BLOCK;
+            if (q < (K >> 3)) {
+                xv[i] = (p.in_kind == IN_NORM) ? src[q] : src[packed_chunk(p.embed_geo, tok, q)];
+                wv[i] = wn[q];
+            }
+        }
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int q = tid + i * MAK_BLOCK;
+            if (q < (K >> 3)) {
+                if (p.in_kind == IN_GATHER_NORM && blockIdx.x == 0)
+                    reinterpret_cast<uint4*>(p.x_store + (size_t)col * p.x_ld)[q] = xv[i];
+                const uint32_t u[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    double a = bf_lo(u[e]), b = bf_hi(u[e]);
+                    const double a = bf_lo(u[e]), b = bf_hi(u[e]);
                     ss = fma(a, a, ss);
                     ss = fma(b, b, ss);
                 }
@@ -94,19 +96,21 @@ __device__ void stage_input(const GemvPhase& p, uint16_t* hs, double* red)
         }
         ss = block_sum(ss, red);
         const float r = rms_scale(ss, K, p.eps);
-        const uint4* wn = reinterpret_cast<const uint4*>(p.norm_w);
-        for (int q = tid; q < (K >> 3); q += MAK_BLOCK) {
-            uint4 v = h4[q], w = wn[q];
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-            uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                uint32_t lo = rms_apply(bf_lo(u[e]), r, bf_lo(ww[e]));
-                uint32_t hi = rms_apply(bf_hi(u[e]), r, bf_hi(ww[e]));
-                o[e] = lo | (hi << 16);
+        for (int i = 0; i < 2; i++) {
+            const int q = tid + i * MAK_BLOCK;
+            if (q < (K >> 3)) {
+                const uint32_t u[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                const uint32_t ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t lo = rms_apply(bf_lo(u[e]), r, bf_lo(ww[e]));
+                    const uint32_t hi = rms_apply(bf_hi(u[e]), r, bf_hi(ww[e]));
+                    o[e] = lo | (hi << 16);
+                }
+                h4[q] = make_uint4(o[0], o[1], o[2], o[3]);
             }
-            h4[q] = make_uint4(o[0], o[1], o[2], o[3]);
         }
         __syncthreads();  // `red` is reused by the next column
     }
@@ -125,9 +129,6 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
     __shared__ int is_last;
     uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
 
-    stage_input<NC>(p, hs, red);
-    __syncthreads();
-
     const int K = p.geo.k;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -137,9 +138,42 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
     const int s = lane & (lr - 1);
     const int G = 64 >> lrl;
     const int J = (K >> 3) >> lrl;
+    const int Q = J * R;                      // 16-byte loads per lane per tile
     const uint4* W = reinterpret_cast<const uint4*>(p.w);
     const int n_waves = gridDim.x * (MAK_BLOCK / 64);
     const int N = p.geo.n_rows;
+    constexpr int D = (NC >= 4) ? 8 : 16;     // loads in flight per lane (multiple of R)
+    static_assert(D % R == 0, "ring depth must be a multiple of R");
+
+    // The weights do not depend on this step's activations: start streaming
+    // the first tile before the input (and its RMSNorm) is staged.
+    int tile = blockIdx.x * (MAK_BLOCK / 64) + wave;
+    uint4 buf[D];
+    if (tile < p.geo.n_tiles) {
+        const uint4* wt = W + (int64_t)tile * Q * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < D; i++)
+            if (i < Q) buf[i] = wt[i * 64];
+    }
+
+    // residual rows of the first tile (lane s == 0 owns rows row0 .. row0+R-1)
+    float xres[R][NC];
+    auto load_res = [&](int t) {
+        if (EPI == EPI_RESIDUAL && s == 0) {
+            const int row0 = t * G * R + grp * R;
+#pragma unroll
+            for (int r = 0; r < R; r++)
+#pragma unroll
+                for (int c = 0; c < NC; c++)
+                    xres[r][c] = (row0 + r < N && c < p.ncols)
+                                     ? bf2f(p.out[(size_t)(p.col0 + c) * p.out_ld + row0 + r])
+                                     : 0.f;
+        }
+    };
+    if (tile < p.geo.n_tiles) load_res(tile);
+
+    stage_input<NC>(p, hs, red);
+    __syncthreads();
 
     float best_v[NC];
     int best_i[NC];
@@ -149,55 +183,74 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
         best_i[c] = 0x7fffffff;
     }
 
-    for (int tile = blockIdx.x * (MAK_BLOCK / 64) + wave; tile < p.geo.n_tiles; tile += n_waves) {
+    for (; tile < p.geo.n_tiles; tile += n_waves) {
         double acc[R][NC];
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
             for (int c = 0; c < NC; c++) acc[r][c] = 0.0;
 
-        const uint4* wt = W + (int64_t)tile * J * R * 64 + lane;
-        uint4 cur[R];
+        const uint4* wt = W + (int64_t)tile * Q * 64 + lane;
+        uint4 hv[NC];
+        constexpr bool kCacheH = NC <= 2;          // keep the input chunk as fp64
+        double hdc[kCacheH ? NC : 1][8];
+        // ring of D loads: slot i holds load q0 + i; load q = j*R + r
+        for (int q0 = 0; q0 < Q; q0 += D) {
 #pragma unroll
-        for (int r = 0; r < R; r++) cur[r] = wt[r * 64];
-        for (int j = 0; j < J; j++) {
-            uint4 nxt[R];
-            if (j + 1 < J) {
+            for (int i = 0; i < D; i++) {
+                const int q = q0 + i;
+                if (q < Q) {
+                    const uint4 w = buf[i];
+                    if (q + D < Q) buf[i] = wt[(q + D) * 64];
+                    constexpr int RR = R;
+                    const int r = i % RR;
+                    if (r == 0) {
+                        const int chunk = ((q / RR) << lrl) + s;
 #pragma unroll
-                for (int r = 0; r < R; r++) nxt[r] = wt[((j + 1) * R + r) * 64];
-            }
-            const int chunk = (j << lrl) + s;
-            uint4 hv[NC];
+                        for (int c = 0; c < NC; c++)
+                            hv[c] = reinterpret_cast<const uint4*>(hs + (size_t)c * K)[chunk];
+                        if (kCacheH) {
 #pragma unroll
-            for (int c = 0; c < NC; c++)
-                hv[c] = reinterpret_cast<const uint4*>(hs + (size_t)c * K)[chunk];
+                            for (int c = 0; c < (kCacheH ? NC : 1); c++) {
+                                const uint32_t hu[4] = {hv[c].x, hv[c].y, hv[c].z, hv[c].w};
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                double hd[NC];
+                                for (int e = 0; e < 8; e++)
+                                    hdc[c][e] = (e & 1) ? bf_hi(hu[e >> 1]) : bf_lo(hu[e >> 1]);
+                            }
+                        }
+                    }
+                    const uint32_t wu[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                for (int c = 0; c < NC; c++) {
-                    const uint32_t hu = (e < 2) ? hv[c].x : (e < 4) ? hv[c].y : (e < 6) ? hv[c].z : hv[c].w;
-                    hd[c] = (e & 1) ? bf_hi(hu) : bf_lo(hu);
+                    for (int e = 0; e < 8; e++) {
+                        const double wd = (e & 1) ? bf_hi(wu[e >> 1]) : bf_lo(wu[e >> 1]);
+#pragma unroll
+                        for (int c = 0; c < NC; c++) {
+                            double hd;
+                            if (kCacheH) {
+                                hd = hdc[kCacheH ? c : 0][e];
+                            } else {
+                                const uint32_t hu = (e < 2) ? hv[c].x : (e < 4) ? hv[c].y : (e < 6) ? hv[c].z : hv[c].w;
+                                hd = (e & 1) ? bf_hi(hu) : bf_lo(hu);
+                            }
+                            acc[r][c] = fma(wd, hd, acc[r][c]);
+                        }
+                    }
                 }
-#pragma unroll
-                for (int r = 0; r < R; r++) {
-                    const uint32_t wu = (e < 2) ? cur[r].x : (e < 4) ? cur[r].y : (e < 6) ? cur[r].z : cur[r].w;
-                    const double wd = (e & 1) ? bf_hi(wu) : bf_lo(wu);
-#pragma unroll
-                    for (int c = 0; c < NC; c++) acc[r][c] = fma(wd, hd[c], acc[r][c]);
-                }
-            }
-            if (j + 1 < J) {
-#pragma unroll
-                for (int r = 0; r < R; r++) cur[r] = nxt[r];
             }
         }
-        // reduce over the lr lanes of each row group (fixed xor tree)
+        // start the next tile's weight stream before reducing this one
+        const int next = tile + n_waves;
+        if (next < p.geo.n_tiles) {
+            const uint4* wn = W + (int64_t)next * Q * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < D; i++)
+                if (i < Q) buf[i] = wn[i * 64];
+        }
+        // reduce over the lr lanes of each row group (fixed tree)
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
-            for (int c = 0; c < NC; c++)
-                for (int o = lr >> 1; o > 0; o >>= 1) acc[r][c] += __shfl_xor(acc[r][c], o, 64);
+            for (int c = 0; c < NC; c++) acc[r][c] = group_sum_rt(acc[r][c], lrl);
 
         if (s == 0) {
             const int row0 = tile * G * R + grp * R;
@@ -230,9 +283,8 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
                         if (EPI == EPI_STORE) {
                             p.out[col * p.out_ld + row] = f2bf((float)acc[r][c]);
                         } else if (EPI == EPI_RESIDUAL) {
-                            uint16_t* xp = p.out + col * p.out_ld + row;
                             const float y = rbf((float)acc[r][c]);
-                            *xp = f2bf(bf2f(*xp) + y);
+                            p.out[col * p.out_ld + row] = f2bf(xres[r][c] + y);
                         } else {  // EPI_LOGITS
                             const float v = (float)acc[r][c];
                             p.logits[(size_t)c * p.logits_ld + row] = v;
@@ -245,6 +297,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
                 }
             }
         }
+        if (EPI == EPI_RESIDUAL && tile + n_waves < p.geo.n_tiles) load_res(tile + n_waves);
     }
 
     if (EPI != EPI_LOGITS) return;
@@ -330,17 +383,18 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
         __syncthreads();
     }
     if (threadIdx.x == 0) {
+        // new column c takes over from column col0 + c >= c, so updating in
+        // ascending order never overwrites a column still to be read
         Ctl* ctl = p.ctl;
-        ColState old[MAK_MAX_COLS];
-        for (int c = 0; c < p.ncols; c++) old[c] = ctl->cols[p.col0 + c];
         const int step = ctl->step;
         for (int c = 0; c < p.ncols; c++) {
+            const ColState old = ctl->cols[p.col0 + c];
             if (p.out_tokens) p.out_tokens[step * p.ncols + c] = next_tok[c];
             ColState ns;
             ns.token = next_tok[c];
-            ns.pos = old[c].pos + 1;
-            ns.slot = old[c].slot;
-            ns.first_pos = old[c].pos + 1;
+            ns.pos = old.pos + 1;
+            ns.slot = old.slot;
+            ns.first_pos = old.pos + 1;
             ns.first_col = c;
             ns.pad_[0] = ns.pad_[1] = ns.pad_[2] = 0;
             ctl->cols[c] = ns;
@@ -355,32 +409,67 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
 // ---------------------------------------------------------------------------
 // attention: one workgroup per (column, kv head)
 // ---------------------------------------------------------------------------
-// LDS layout (dynamic): qf[rep][d] f32 | kin[n_in][d] bf16 | vin[n_in][d] bf16 |
-//                       S[rep][max_seq] bf16
+// For the column's q heads of kv group g: per-head qk RMSNorm, rope at the
+// column's position, append of this column's k', v at that position, then
+// softmax(q'K^T * scale) V over positions 0..pos.  Positions before the first
+// column of this sequence in the step come from the KV cache; the step's own
+// earlier columns (a prefill chunk) come from LDS, so no workgroup reads a
+// cache row another one writes in the same launch.
+//
+// Lanes split a K/V row into 16-byte chunks (LP = d/8 lanes per row); rows
+// spread over lane groups and the 4 waves; each lane keeps U rows in flight.
+// D_ / REP_ fix head_dim and q heads per kv head at compile time (0 = runtime).
+//
+// LDS (dynamic): pv[16][d] f64 | qf[rep][d] f32 | kin[8][d] bf16 |
+//                vin[8][d] bf16 | S[rep][max_seq] f32
+template <int D_, int REP_>
 __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ double red[4];
-    __shared__ float fred[4];
-    __shared__ float mx[32];
-    __shared__ float zs[32];
-
-    const int Hq = p.n_q_heads, Hkv = p.n_kv_heads, d = p.head_dim, half = d >> 1;
-    const int rep = Hq / Hkv;
+    const int d = D_ > 0 ? D_ : p.head_dim;
+    const int rep = REP_ > 0 ? REP_ : p.n_q_heads / p.n_kv_heads;
+    constexpr int HG = (REP_ > 0 && REP_ < 4) ? REP_ : 4;   // heads per P.V pass
+    const int Hq = p.n_q_heads, Hkv = p.n_kv_heads, half = d >> 1;
     const int col = blockIdx.x / Hkv;
     const int g = blockIdx.x - col * Hkv;
-    const ColState cs = p.ctl->cols[col];
-    const int pos = cs.pos, fp = cs.first_pos, n = pos + 1, n_in = pos - fp + 1;
     const int q_dim = Hq * d, kv_dim = Hkv * d;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    float* qf = reinterpret_cast<float*>(smem);
+    double* pv = reinterpret_cast<double*>(smem);
+    float* qf = reinterpret_cast<float*>(pv + 16 * d);
     uint16_t* kin = reinterpret_cast<uint16_t*>(qf + rep * d);
     uint16_t* vin = kin + MAK_MAX_COLS * d;
-    uint16_t* S = vin + MAK_MAX_COLS * d;
+    float* S = reinterpret_cast<float*>(vin + MAK_MAX_COLS * d);
 
-    // stage A: raw q heads of this group, raw k/v of every in-step column of
-    // this sequence up to this one
+    const int lp_log2 = __builtin_ctz(d >> 3);
+    const int LP = 1 << lp_log2;
+    const int rows_w = 64 >> lp_log2;
+    const int rows_it = 4 * rows_w;
+    const int sub = lane >> lp_log2, ch = lane & (LP - 1);
+    const int my_row = wave * rows_w + sub;
+    constexpr int U = 4;
+
+    // ---- round trip 1: this column's state
+    const ColState cs = p.ctl->cols[col];
+    const int pos = cs.pos, fp = cs.first_pos, n = pos + 1, n_in = pos - fp + 1;
+    const size_t head_base = ((size_t)cs.slot * Hkv + g) * p.max_seq;
+    const uint16_t* kc_h = p.kc + head_base * d;
+    const uint16_t* vc_h = p.vc + head_base * d;
+
+    // ---- round trip 2: everything else at once.  First the leading cached
+    // K and V rows (they do not depend on this step) ...
+    uint4 kpre[U], vpre[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int j = u * rows_it + my_row;
+        kpre[u] = make_uint4(0, 0, 0, 0);
+        vpre[u] = make_uint4(0, 0, 0, 0);
+        if (j < fp) {
+            kpre[u] = *reinterpret_cast<const uint4*>(kc_h + (size_t)j * d + ch * 8);
+            vpre[u] = *reinterpret_cast<const uint4*>(vc_h + (size_t)j * d + ch * 8);
+        }
+    }
+    // ... then the raw q heads and the step's k/v rows of this sequence
     for (int t = tid; t < rep * d; t += MAK_BLOCK) {
         const int h = t / d, i = t - h * d;
         qf[t] = bf2f(p.qkv[(size_t)col * p.qkv_ld + (g * rep + h) * d + i]);
@@ -393,7 +482,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
     }
     __syncthreads();
 
-    // stage B: per-head qk RMSNorm (one wave per vector)
+    // per-head qk RMSNorm (one wave per vector)
     if (p.q_norm) {
         for (int vi = wave; vi < rep + n_in; vi += 4) {
             double ss = 0.0;
@@ -416,7 +505,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
         __syncthreads();
     }
 
-    // stage C: rope (pairs i, i + d/2), q at pos, in-step k at fp + ci
+    // rope (pairs i, i + d/2): q at pos, the step's k rows at fp + ci
     for (int t = tid; t < (rep + n_in) * half; t += MAK_BLOCK) {
         const int vi = t / half, i = t - vi * half;
         const int at = (vi < rep) ? pos : fp + (vi - rep);
@@ -435,75 +524,124 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
     }
     __syncthreads();
 
-    // stage D: append this column's k', v at pos
-    const size_t head_base = ((size_t)cs.slot * Hkv + g) * p.max_seq;
+    // append this column's k', v at pos (single owner: this workgroup)
     for (int i = tid; i < d; i += MAK_BLOCK) {
         p.kc[(head_base + pos) * d + i] = kin[(n_in - 1) * d + i];
         p.vc[(head_base + pos) * d + i] = vin[(n_in - 1) * d + i];
     }
 
-    // stage E: scores sigma_j = bf16(bf16(q'.K_j) * scale), j <= pos
-    for (int j = tid; j < n; j += MAK_BLOCK) {
-        const uint16_t* kr = (j < fp) ? p.kc + (head_base + j) * d : kin + (j - fp) * d;
-        for (int h = 0; h < rep; h++) {
-            double acc = 0.0;
-            for (int i = 0; i < d; i += 8) {
-                const uint4 kv = *reinterpret_cast<const uint4*>(kr + i);
-                const uint32_t u[4] = {kv.x, kv.y, kv.z, kv.w};
+    // scores sigma_j = bf16(bf16(q'.K_j) * scale)
+    for (int j0 = 0; j0 < n; j0 += U * rows_it) {
+        uint4 kv[U];
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    acc = fma((double)qf[h * d + i + 2 * e], (double)bf_lo(u[e]), acc);
-                    acc = fma((double)qf[h * d + i + 2 * e + 1], (double)bf_hi(u[e]), acc);
-                }
-            }
-            S[h * p.max_seq + j] = f2bf(rbf((float)acc) * p.scale);
+        for (int u = 0; u < U; u++) {
+            const int j = j0 + u * rows_it + my_row;
+            if (j0 == 0) kv[u] = kpre[u];
+            else kv[u] = (j < fp) ? *reinterpret_cast<const uint4*>(kc_h + (size_t)j * d + ch * 8)
+                                  : make_uint4(0, 0, 0, 0);
+            if (j >= fp && j < n) kv[u] = *reinterpret_cast<const uint4*>(kin + (j - fp) * d + ch * 8);
         }
-    }
-    // per-head max (each thread first scans the scores it wrote itself)
-    for (int h = 0; h < rep; h++) {
-        float v = -INFINITY;
-        for (int j = tid; j < n; j += MAK_BLOCK) v = fmaxf(v, bf2f(S[h * p.max_seq + j]));
-        v = block_max(v, fred);
-        if (tid == 0) mx[h] = v;
-    }
-    __syncthreads();
-    for (int h = 0; h < rep; h++) {
-        const float m = mx[h];
-        double z = 0.0;
-        for (int j = tid; j < n; j += MAK_BLOCK)
-            z += (double)(float)exp((double)bf2f(S[h * p.max_seq + j]) - (double)m);
-        z = block_sum(z, red);
-        if (tid == 0) zs[h] = (float)z;
-    }
-    __syncthreads();
-    // probabilities P_j = bf16(fp32(e_j / Z)) replace the scores
-    for (int h = 0; h < rep; h++) {
-        const double m = mx[h], z = zs[h];
-        for (int j = tid; j < n; j += MAK_BLOCK) {
-            uint16_t* sp = &S[h * p.max_seq + j];
-            const double e = (double)(float)exp((double)bf2f(*sp) - m);
-            *sp = f2bf((float)(e / z));
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int j = j0 + u * rows_it + my_row;
+            const uint32_t ku[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+            double kd[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) kd[e] = (e & 1) ? bf_hi(ku[e >> 1]) : bf_lo(ku[e >> 1]);
+#pragma unroll(REP_ > 0 ? REP_ : 1)
+            for (int h = 0; h < rep; h++) {
+                const float4 qa = *reinterpret_cast<const float4*>(qf + h * d + ch * 8);
+                const float4 qb = *reinterpret_cast<const float4*>(qf + h * d + ch * 8 + 4);
+                const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+                double part = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; e++) part = fma((double)qv[e], kd[e], part);
+                part = (D_ > 0) ? group_sum<(D_ > 0 ? __builtin_ctz(D_ >> 3) : 0)>(part)
+                                : group_sum_rt(part, lp_log2);
+                if (ch == 0 && j < n) S[h * p.max_seq + j] = rbf(rbf((float)part) * p.scale);
+            }
         }
     }
     __syncthreads();
 
-    // stage I: o_h[i] = bf16(sum_j P_j V_j[i])
-    for (int t = tid; t < rep * d; t += MAK_BLOCK) {
-        const int h = t / d, i = t - h * d;
-        const uint16_t* Ph = S + h * p.max_seq;
-        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-        const int nc = (fp < n) ? fp : n;  // cached positions
-        int j = 0;
-        for (; j + 4 <= nc; j += 4) {
-            a0 = fma((double)bf2f(Ph[j]), (double)bf2f(p.vc[(head_base + j) * d + i]), a0);
-            a1 = fma((double)bf2f(Ph[j + 1]), (double)bf2f(p.vc[(head_base + j + 1) * d + i]), a1);
-            a2 = fma((double)bf2f(Ph[j + 2]), (double)bf2f(p.vc[(head_base + j + 2) * d + i]), a2);
-            a3 = fma((double)bf2f(Ph[j + 3]), (double)bf2f(p.vc[(head_base + j + 3) * d + i]), a3);
+    // softmax of each head inside one wave: max, e_j = fp32(exp(sigma_j - max)),
+    // Z = fp32(sum e_j), P_j = bf16(fp32(e_j / Z)); a lane rewrites only the
+    // entries it reads
+    for (int h = wave; h < rep; h += 4) {
+        float* Sh = S + h * p.max_seq;
+        float m = -INFINITY;
+        for (int j = lane; j < n; j += 64) m = fmaxf(m, Sh[j]);
+        m = wave_max(m);
+        double z = 0.0;
+        for (int j = lane; j < n; j += 64) {
+            const float e = (float)exp((double)Sh[j] - (double)m);
+            Sh[j] = e;
+            z += (double)e;
         }
-        for (; j < nc; j++) a0 = fma((double)bf2f(Ph[j]), (double)bf2f(p.vc[(head_base + j) * d + i]), a0);
-        for (; j < n; j++) a1 = fma((double)bf2f(Ph[j]), (double)bf2f(vin[(j - fp) * d + i]), a1);
-        const double acc = (a0 + a1) + (a2 + a3);
-        p.o[(size_t)col * q_dim + (g * rep + h) * d + i] = f2bf((float)acc);
+        const double Z = (double)(float)wave_sum(z);
+        for (int j = lane; j < n; j += 64) Sh[j] = rbf((float)((double)Sh[j] / Z));
+    }
+    __syncthreads();
+
+    // o_h = bf16(sum_j P_j V_j): per-lane partial sums over its rows, folded
+    // across lane groups, then across waves (in wave order) through LDS
+    for (int h0 = 0; h0 < rep; h0 += HG) {
+        double acc[HG][8];
+#pragma unroll
+        for (int hh = 0; hh < HG; hh++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[hh][e] = 0.0;
+        for (int j0 = 0; j0 < n; j0 += U * rows_it) {
+            uint4 vv[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int j = j0 + u * rows_it + my_row;
+                if (j0 == 0) vv[u] = vpre[u];
+                else vv[u] = (j < fp) ? *reinterpret_cast<const uint4*>(vc_h + (size_t)j * d + ch * 8)
+                                      : make_uint4(0, 0, 0, 0);
+                if (j >= fp && j < n) vv[u] = *reinterpret_cast<const uint4*>(vin + (j - fp) * d + ch * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int j = j0 + u * rows_it + my_row;
+                if (j >= n) continue;
+                const uint32_t vu[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+#pragma unroll
+                for (int hh = 0; hh < HG; hh++) {
+                    if (h0 + hh >= rep) break;
+                    const double pj = (double)S[(h0 + hh) * p.max_seq + j];
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        acc[hh][e] = fma(pj, (double)((e & 1) ? bf_hi(vu[e >> 1]) : bf_lo(vu[e >> 1])), acc[hh][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < HG; hh++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                if (D_ > 0) {
+                    acc[hh][e] = stride_sum<(D_ > 0 ? __builtin_ctz(D_ >> 3) : 1)>(acc[hh][e]);
+                } else {
+                    for (int o = LP; o < 64; o <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
+                }
+            }
+        if (sub == 0) {
+#pragma unroll
+            for (int hh = 0; hh < HG; hh++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) pv[(wave * 4 + hh) * d + ch * 8 + e] = acc[hh][e];
+        }
+        __syncthreads();
+        for (int t = tid; t < HG * d; t += MAK_BLOCK) {
+            const int hh = t / d, i = t - hh * d;
+            if (h0 + hh < rep) {
+                const double v = ((pv[(0 * 4 + hh) * d + i] + pv[(1 * 4 + hh) * d + i]) +
+                                  pv[(2 * 4 + hh) * d + i]) + pv[(3 * 4 + hh) * d + i];
+                p.o[(size_t)col * q_dim + (g * rep + h0 + hh) * d + i] = f2bf((float)v);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -573,16 +711,33 @@ hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
+// dynamic LDS of k_attn: pv[16][d] f64 | qf[rep][d] f32 | kin, vin [8][d] bf16 | S[rep][max_seq] f32
+size_t mak_attn_lds_for(int rep, int d, int max_seq)
+{
+    return (size_t)16 * d * 8 + (size_t)rep * d * 4 + 2 * (size_t)MAK_MAX_COLS * d * 2 +
+           (size_t)rep * max_seq * 4;
+}
+
 size_t mak_attn_lds(const AttnPhase& p)
 {
-    const int rep = p.n_q_heads / p.n_kv_heads;
-    return (size_t)rep * p.head_dim * 4 + 2 * (size_t)MAK_MAX_COLS * p.head_dim * 2 +
-           (size_t)rep * p.max_seq * 2;
+    return mak_attn_lds_for(p.n_q_heads / p.n_kv_heads, p.head_dim, p.max_seq);
 }
+
+#define MAK_ATTN_SHAPES(X) X(32, 3) X(64, 2) X(64, 3) X(64, 4) X(64, 8) X(128, 2) X(128, 4)
 
 hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_attn, dim3(p.ncols * p.n_kv_heads), dim3(MAK_BLOCK), mak_attn_lds(p), st, p);
+    const dim3 grid(p.ncols * p.n_kv_heads), block(MAK_BLOCK);
+    const size_t lds = mak_attn_lds(p);
+    const int rep = p.n_q_heads / p.n_kv_heads;
+#define X(D, REP)                                                                  \
+    if (p.head_dim == D && rep == REP) {                                           \
+        hipLaunchKernelGGL((k_attn<D, REP>), grid, block, lds, st, p);           \
+        return hipGetLastError();                                                  \
+    }
+    MAK_ATTN_SHAPES(X)
+#undef X
+    hipLaunchKernelGGL((k_attn<0, 0>), grid, block, lds, st, p);
     return hipGetLastError();
 }
 
@@ -596,8 +751,9 @@ hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int ste
     return hipGetLastError();
 }
 
-// Raise the dynamic-LDS ceiling of every kernel instantiation to `bytes`.
-hipError_t mak_set_lds_limit(int bytes)
+// Raise the dynamic-LDS ceiling of the GEMV instantiations to `bytes` and of
+// the attention kernel to `attn_bytes`.
+hipError_t mak_set_lds_limit(int bytes, int attn_bytes)
 {
 #define SETA(R, NC, E)                                                                          \
     do {                                                                                        \
@@ -610,9 +766,17 @@ hipError_t mak_set_lds_limit(int bytes)
     SETN(1);
     SETN(2);
     SETN(4);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    return e;
+#define X(D, REP)                                                                          \
+    {                                                                                      \
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D, REP>),  \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                                           attn_bytes);                                    \
+        if (e != hipSuccess) return e;                                                     \
+    }
+    MAK_ATTN_SHAPES(X)
+#undef X
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<0, 0>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, attn_bytes);
 #undef SETA
 #undef SETE
 #undef SETN

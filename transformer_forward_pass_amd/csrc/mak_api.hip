@@ -25,7 +25,8 @@
 hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st);
 hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st);
 hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st);
-hipError_t mak_set_lds_limit(int bytes);
+hipError_t mak_set_lds_limit(int bytes, int attn_bytes);
+size_t mak_attn_lds_for(int rep, int d, int max_seq);
 size_t mak_attn_lds(const AttnPhase& p);
 int mak_gemv_nc(int ncols);
 
@@ -53,7 +54,8 @@ int fail(int code, const char* fmt, ...)
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxGemvBlocks = 1024;      // grid cap of a GEMV phase (waves loop over tiles)
-constexpr int kLdsBudget = 60 * 1024;     // dynamic LDS per workgroup we rely on (static LDS < 4 KiB)
+constexpr int kLdsBudget = 60 * 1024;      // GEMV dynamic LDS per workgroup (static LDS < 4 KiB)
+constexpr int kAttnLdsBudget = 150 * 1024; // attention dynamic LDS (gfx950: 160 KiB per workgroup)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -160,8 +162,8 @@ int validate_cfg(const mak_config* c)
         return fail(MAK_EINVAL, "non-positive dimension in cfg");
     if (c->hidden % 8 || c->intermediate % 8 || (c->n_q_heads * c->head_dim) % 8)
         return fail(MAK_EINVAL, "hidden, intermediate and q_dim must be multiples of 8");
-    if (c->head_dim % 8 || c->head_dim > 256)
-        return fail(MAK_EINVAL, "head_dim must be a multiple of 8 and <= 256");
+    if (c->head_dim < 16 || c->head_dim > 256 || (c->head_dim & (c->head_dim - 1)))
+        return fail(MAK_EINVAL, "head_dim must be a power of two in [16, 256]");
     if (c->n_q_heads % c->n_kv_heads)
         return fail(MAK_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
     if (c->n_q_heads / c->n_kv_heads > 32)
@@ -171,12 +173,10 @@ int validate_cfg(const mak_config* c)
     if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0f))
         return fail(MAK_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
     if (c->max_seq > (1 << 20)) return fail(MAK_EINVAL, "max_seq too large");
-    const size_t attn_lds = (size_t)(c->n_q_heads / c->n_kv_heads) * c->head_dim * 4 +
-                            (size_t)4 * MAK_MAX_COLS * c->head_dim +
-                            (size_t)(c->n_q_heads / c->n_kv_heads) * c->max_seq * 2;
-    if (attn_lds > (size_t)kLdsBudget)
+    const size_t attn_lds = mak_attn_lds_for(c->n_q_heads / c->n_kv_heads, c->head_dim, c->max_seq);
+    if (attn_lds > (size_t)kAttnLdsBudget)
         return fail(MAK_EINVAL, "attention workspace (%zu B of LDS) exceeds %d B: lower max_seq",
-                    attn_lds, kLdsBudget);
+                    attn_lds, kAttnLdsBudget);
     return MAK_OK;
 }
 
@@ -242,20 +242,88 @@ uint16_t host_bf16(float f)
 
 }  // namespace
 
+struct PhaseTiming {
+    bool on = false;
+    struct Pending {
+        hipEvent_t a, b;
+        int kind;
+    };
+    std::vector<hipEvent_t> pool;
+    std::vector<Pending> pending;
+    double ms[MAK_PHASE_COUNT] = {};
+    int64_t launches[MAK_PHASE_COUNT] = {};
+};
+
+// A captured step: (ncols, lm_begin, lm_count) -> executable graph.
+struct StepGraph {
+    int ncols, lm_begin, lm_count;
+    hipGraphExec_t exec;
+};
+
 struct mak_model {
     mak_config cfg;
+    PhaseTiming tm;
+    hipStream_t cur = nullptr;       // stream the phase launches go to (capture or model stream)
+    hipStream_t capture = nullptr;   // private stream used only to capture step graphs
+    bool use_graphs = true;
+    std::vector<StepGraph> graphs;
     Layout L;
     char* arena;
     size_t arena_bytes;
     hipStream_t stream;
     std::vector<int32_t> slot_len;   // cached positions per slot
-    int gemv_blocks_cap;
-    int max_cols_by_k[2];            // unused for now
     template <class T>
     T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
 };
 
 namespace {
+
+hipEvent_t take_event(mak_model* m)
+{
+    if (!m->tm.pool.empty()) {
+        hipEvent_t e = m->tm.pool.back();
+        m->tm.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch through `fn` (returns hipError_t); with phase timing on, bracket
+// the launch with events on the model's stream.
+template <class F>
+int launch(mak_model* m, int kind, F&& fn)
+{
+    hipEvent_t a = nullptr, b = nullptr;
+    if (m->tm.on) {
+        a = take_event(m);
+        b = take_event(m);
+        if (!a || !b) return fail(MAK_EDEVICE, "hipEventCreate failed");
+        HIP_TRY(hipEventRecord(a, m->cur));
+    }
+    HIP_TRY(fn());
+    if (m->tm.on) {
+        HIP_TRY(hipEventRecord(b, m->cur));
+        m->tm.pending.push_back({a, b, kind});
+    }
+    return MAK_OK;
+}
+
+// After the stream has drained: fold pending event pairs into the totals.
+int collect_timing(mak_model* m)
+{
+    for (auto& p : m->tm.pending) {
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, p.a, p.b));
+        m->tm.ms[p.kind] += ms;
+        m->tm.launches[p.kind] += 1;
+        m->tm.pool.push_back(p.a);
+        m->tm.pool.push_back(p.b);
+    }
+    m->tm.pending.clear();
+    return MAK_OK;
+}
 
 // Blocks of a GEMV phase: one wave per tile up to the cap.
 int gemv_blocks(const PackGeom& g)
@@ -275,7 +343,7 @@ int max_cols_for_k(int k)
     return 1;
 }
 
-int run_gemv(mak_model* m, GemvPhase p, int ncols, int col0)
+int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
 {
     // split the columns into groups whose inputs fit in LDS
     const int step = (p.epi == EPI_LOGITS) ? ncols : max_cols_for_k(p.geo.k);
@@ -293,14 +361,16 @@ int run_gemv(mak_model* m, GemvPhase p, int ncols, int col0)
             (size_t)mak_gemv_nc(q.ncols) * q.geo.k * 2 > (size_t)kLdsBudget ||
             (q.epi == EPI_SWIGLU && (q.geo.r % 2)))
             return fail(MAK_EINVAL, "internal: bad GEMV phase");
-        HIP_TRY(mak_launch_gemv(q, m->stream));
+        int rc = launch(m, kind, [&] { return mak_launch_gemv(q, m->cur); });
+        if (rc) return rc;
     }
     return MAK_OK;
 }
 
-// One step of the program for the columns currently in the control block:
-// ncols columns; LM head (with argmax feedback) for [lm_begin, lm_begin+lm_count).
-int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens)
+// Launch one step of the program on m->cur for the columns currently in the
+// control block: ncols columns; LM head (with argmax feedback) for
+// [lm_begin, lm_begin + lm_count).
+int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens)
 {
     const mak_config& c = m->cfg;
     const Layout& L = m->L;
@@ -331,7 +401,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         p.out = qkv;
         p.out_ld = L.qkv_ld;
         p.ctl = ctl;
-        if ((rc = run_gemv(m, p, ncols, 0))) return rc;
+        if ((rc = run_gemv(m, MAK_PHASE_QKV, p, ncols, 0))) return rc;
 
         // attention
         AttnPhase a{};
@@ -352,8 +422,8 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         a.max_seq = c.max_seq;
         a.eps = c.rms_eps;
         a.scale = (float)(1.0 / std::sqrt((double)d));
-        if (mak_attn_lds(a) > (size_t)kLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
-        HIP_TRY(mak_launch_attn(a, m->stream));
+        if (mak_attn_lds(a) > (size_t)kAttnLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
+        if ((rc = launch(m, MAK_PHASE_ATTN, [&] { return mak_launch_attn(a, m->cur); }))) return rc;
 
         // O + residual
         GemvPhase po{};
@@ -366,7 +436,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         po.out = x;
         po.out_ld = H;
         po.ctl = ctl;
-        if ((rc = run_gemv(m, po, ncols, 0))) return rc;
+        if ((rc = run_gemv(m, MAK_PHASE_O, po, ncols, 0))) return rc;
 
         // RMSNorm + gate/up + SwiGLU
         GemvPhase pg{};
@@ -381,7 +451,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         pg.out = mm;
         pg.out_ld = c.intermediate;
         pg.ctl = ctl;
-        if ((rc = run_gemv(m, pg, ncols, 0))) return rc;
+        if ((rc = run_gemv(m, MAK_PHASE_GATEUP, pg, ncols, 0))) return rc;
 
         // down + residual
         GemvPhase pd{};
@@ -394,7 +464,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         pd.out = x;
         pd.out_ld = H;
         pd.ctl = ctl;
-        if ((rc = run_gemv(m, pd, ncols, 0))) return rc;
+        if ((rc = run_gemv(m, MAK_PHASE_DOWN, pd, ncols, 0))) return rc;
     }
     if (lm_count > 0) {
         GemvPhase p{};
@@ -416,16 +486,52 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         p.part_idx = m->at<int32_t>(L.part_idx);
         p.out_tokens = d_out_tokens;
         p.ctl = ctl;
-        int rc = run_gemv(m, p, lm_count, lm_begin);
+        int rc = run_gemv(m, MAK_PHASE_LMHEAD, p, lm_count, lm_begin);
         if (rc) return rc;
     }
     return MAK_OK;
 }
 
+// Run one step: replay (capturing on first use) the step's graph on the
+// model's stream, or launch the phases one by one when graphs are off or
+// phase timing is on.  The step reads its per-call state (tokens, positions,
+// slots) from the control block, so one graph serves every step of a shape.
+int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens)
+{
+    if (!m->use_graphs || m->tm.on) {
+        m->cur = m->stream;
+        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens);
+    }
+    for (const StepGraph& g : m->graphs)
+        if (g.ncols == ncols && g.lm_begin == lm_begin && g.lm_count == lm_count) {
+            HIP_TRY(hipGraphLaunch(g.exec, m->stream));
+            return MAK_OK;
+        }
+    hipGraph_t graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal));
+    m->cur = m->capture;
+    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens);
+    hipError_t e = hipStreamEndCapture(m->capture, &graph);
+    m->cur = m->stream;
+    if (rc) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (e != hipSuccess) return fail(MAK_EDEVICE, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    StepGraph sg{ncols, lm_begin, lm_count, nullptr};
+    e = hipGraphInstantiate(&sg.exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(MAK_EDEVICE, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    m->graphs.push_back(sg);
+    HIP_TRY(hipGraphLaunch(sg.exec, m->stream));
+    return MAK_OK;
+}
+
 int set_cols(mak_model* m, const ColState* cols, int ncols, int step)
 {
-    HIP_TRY(mak_launch_set_ctl(m->at<Ctl>(m->L.ctl), cols, ncols, step, m->stream));
-    return MAK_OK;
+    m->cur = m->stream;
+    return launch(m, MAK_PHASE_CTL,
+                  [&] { return mak_launch_set_ctl(m->at<Ctl>(m->L.ctl), cols, ncols, step, m->stream); });
 }
 
 // Consume ids[0..n) of `slot` from start_pos; LM head on the last token when
@@ -501,7 +607,7 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
         return fail(MAK_ENOMEM, "arena has %zu bytes, needs %zu", arena_bytes, L.total);
 
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    HIP_TRY(mak_set_lds_limit(kLdsBudget));
+    HIP_TRY(mak_set_lds_limit(kLdsBudget, kAttnLdsBudget));
     char* A = reinterpret_cast<char*>(d_arena);
     const int H = c.hidden, d = c.head_dim, I = c.intermediate;
     const int q_dim = c.n_q_heads * d, kv_dim = c.n_kv_heads * d;
@@ -565,6 +671,11 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
     m->arena_bytes = arena_bytes;
     m->stream = st;
     m->slot_len.assign(c.max_batch, 0);
+    m->cur = st;
+    if (hipStreamCreateWithFlags(&m->capture, hipStreamNonBlocking) != hipSuccess) {
+        delete m;
+        return fail(MAK_EDEVICE, "hipStreamCreateWithFlags failed");
+    }
     *out = m;
     g_err.clear();
     return MAK_OK;
@@ -604,7 +715,52 @@ int mak_read_kv(const mak_model* m, int32_t layer, int32_t slot, int32_t pos0, i
     return MAK_OK;
 }
 
-void mak_free(mak_model* m) { delete m; }
+int mak_set_executor(mak_model* m, int executor)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    if (executor != MAK_EXEC_GRAPH && executor != MAK_EXEC_PHASED)
+        return fail(MAK_EINVAL, "unknown executor %d", executor);
+    m->use_graphs = executor == MAK_EXEC_GRAPH;
+    return MAK_OK;
+}
+
+int mak_set_phase_timing(mak_model* m, int enable)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    if ((rc = collect_timing(m))) return rc;
+    m->tm.on = enable != 0;
+    if (m->tm.on) {
+        for (int k = 0; k < MAK_PHASE_COUNT; k++) {
+            m->tm.ms[k] = 0.0;
+            m->tm.launches[k] = 0;
+        }
+    }
+    return MAK_OK;
+}
+
+int mak_phase_times(const mak_model* m, double* ms, int64_t* launches)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    for (int k = 0; k < MAK_PHASE_COUNT; k++) {
+        if (ms) ms[k] = m->tm.ms[k];
+        if (launches) launches[k] = m->tm.launches[k];
+    }
+    return MAK_OK;
+}
+
+void mak_free(mak_model* m)
+{
+    if (!m) return;
+    if (hipStreamSynchronize(m->stream) == hipSuccess) collect_timing(m);
+    for (hipEvent_t e : m->tm.pool) (void)hipEventDestroy(e);
+    for (StepGraph& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    if (m->capture) (void)hipStreamDestroy(m->capture);
+    delete m;
+}
 
 int mak_prefill(mak_model* m, int32_t slot, const int32_t* ids, int32_t n, int32_t start_pos,
                 float* d_logits)
@@ -625,6 +781,7 @@ int mak_prefill(mak_model* m, int32_t slot, const int32_t* ids, int32_t n, int32
         HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)c.vocab * 4,
                                hipMemcpyDeviceToDevice, m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
+    if ((rc = collect_timing(m))) return rc;
     m->slot_len[slot] = start_pos + n;
     return MAK_OK;
 }
@@ -655,6 +812,7 @@ int mak_decode_step(mak_model* m, int32_t slot, int32_t token, int32_t pos, floa
         HIP_TRY(hipMemcpyAsync(next_token, m->at<int32_t>(m->L.out_tokens), 4, hipMemcpyDeviceToHost,
                                m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
+    if ((rc = collect_timing(m))) return rc;
     m->slot_len[slot] = pos + 1;
     return MAK_OK;
 }
@@ -679,6 +837,7 @@ int mak_generate(mak_model* m, int32_t slot, const int32_t* prompt, int32_t n, i
         if ((rc = run_step(m, 1, 0, 1, d_out))) return rc;
     HIP_TRY(hipMemcpyAsync(out_tokens, d_out, (size_t)max_new * 4, hipMemcpyDeviceToHost, m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
+    if ((rc = collect_timing(m))) return rc;
     m->slot_len[slot] = n + max_new - 1;
     return MAK_OK;
 }
@@ -719,6 +878,7 @@ int mak_decode_batch(mak_model* m, int32_t B, const int32_t* slots, const int32_
         HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)B * c.vocab * 4,
                                hipMemcpyDeviceToDevice, m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
+    if ((rc = collect_timing(m))) return rc;
     for (int b = 0; b < B; b++) m->slot_len[slots[b]] = positions[b] + steps;
     return MAK_OK;
 }

@@ -21,8 +21,10 @@ MAK_MAX_BATCH = 8
 MAK_PREFILL_CHUNK = 8
 
 EXPORTS = ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_generate",
-           "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_free",
-           "mak_last_error")
+           "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",
+           "mak_set_phase_timing", "mak_phase_times", "mak_free", "mak_last_error")
+EXEC_GRAPH, EXEC_PHASED = 0, 1
+PHASES = ("qkv", "attn", "o", "gateup", "down", "lmhead", "ctl")
 
 
 class MakError(RuntimeError):
@@ -75,11 +77,15 @@ def lib():
         L.mak_batch_max.argtypes = [P]
         L.mak_slot_length.argtypes = [P, I32]
         L.mak_read_kv.argtypes = [P, I32, I32, I32, I32, P, P]
+        L.mak_set_executor.argtypes = [P, ctypes.c_int]
+        L.mak_set_phase_timing.argtypes = [P, ctypes.c_int]
+        L.mak_phase_times.argtypes = [P, P, P]
         L.mak_free.argtypes = [P]
         L.mak_free.restype = None
         L.mak_last_error.restype = ctypes.c_char_p
         for n in ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_generate",
-                  "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv"):
+                  "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",
+                  "mak_set_phase_timing", "mak_phase_times"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +211,20 @@ class MakModel:
         _check(lib().mak_read_kv(self.h, layer, slot, pos0, n, k.ctypes.data, v.ctypes.data))
         f = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         return f(k), f(v)
+
+    def set_executor(self, executor: int):
+        """EXEC_GRAPH (captured step graphs) or EXEC_PHASED (one launch per phase)."""
+        _check(lib().mak_set_executor(self.h, int(executor)))
+
+    def set_phase_timing(self, enable: bool):
+        _check(lib().mak_set_phase_timing(self.h, int(enable)))
+
+    def phase_times(self) -> dict:
+        """{phase: (total ms, launches)} accumulated while timing was on."""
+        ms = np.zeros(len(PHASES), np.float64)
+        n = np.zeros(len(PHASES), np.int64)
+        _check(lib().mak_phase_times(self.h, ms.ctypes.data, n.ctypes.data))
+        return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(PHASES)}
 
     def free(self):
         if getattr(self, "h", None) is not None and self.h.value:
