@@ -49,7 +49,7 @@ extern "C" {
 #define MAK_MAX_BATCH 8     /* columns of one decode batch                          */
 #define MAK_PREFILL_CHUNK 8 /* prompts are consumed in chunks of at most 8 tokens    */
 
-/* Model shape.  head_dim even and <= 256; hidden, intermediate and
+/* Model shape.  head_dim a power of two in [16, 128]; hidden, intermediate and
  * n_q_heads*head_dim multiples of 8; n_q_heads a multiple of n_kv_heads;
  * 1 <= max_batch <= MAK_MAX_BATCH; max_seq >= 1. */
 typedef struct {

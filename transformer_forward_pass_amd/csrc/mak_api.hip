@@ -29,6 +29,7 @@ hipError_t mak_set_lds_limit(int bytes, int attn_bytes);
 size_t mak_attn_lds_for(int rep, int d, int max_seq);
 size_t mak_attn_lds(const AttnPhase& p);
 int mak_gemv_nc(int ncols);
+int mak_gemv_blocks(const GemvPhase& p, int cap);
 
 namespace {
 
@@ -162,8 +163,8 @@ int validate_cfg(const mak_config* c)
         return fail(MAK_EINVAL, "non-positive dimension in cfg");
     if (c->hidden % 8 || c->intermediate % 8 || (c->n_q_heads * c->head_dim) % 8)
         return fail(MAK_EINVAL, "hidden, intermediate and q_dim must be multiples of 8");
-    if (c->head_dim < 16 || c->head_dim > 256 || (c->head_dim & (c->head_dim - 1)))
-        return fail(MAK_EINVAL, "head_dim must be a power of two in [16, 256]");
+    if (c->head_dim < 16 || c->head_dim > 128 || (c->head_dim & (c->head_dim - 1)))
+        return fail(MAK_EINVAL, "head_dim must be a power of two in [16, 128]");
     if (c->n_q_heads % c->n_kv_heads)
         return fail(MAK_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
     if (c->n_q_heads / c->n_kv_heads > 32)
@@ -325,14 +326,6 @@ int collect_timing(mak_model* m)
     return MAK_OK;
 }
 
-// Blocks of a GEMV phase: one wave per tile up to the cap.
-int gemv_blocks(const PackGeom& g)
-{
-    const int waves = MAK_BLOCK / 64;
-    int b = (g.n_tiles + waves - 1) / waves;
-    return std::max(1, std::min(b, kMaxGemvBlocks));
-}
-
 // Largest column group whose bf16 input rows fit the LDS budget.
 int max_cols_for_k(int k)
 {
@@ -353,7 +346,7 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
         GemvPhase q = p;
         q.col0 = col0 + c0;
         q.ncols = std::min(step, ncols - c0);
-        q.n_blocks = gemv_blocks(q.geo);
+        q.n_blocks = mak_gemv_blocks(q, kMaxGemvBlocks);
         if (q.epi == EPI_LOGITS && q.col0 != col0)
             return fail(MAK_EINVAL, "internal: LM head split");
         // host-side shape checks of what the kernel assumes

@@ -65,6 +65,9 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libmak.so is not built (run __graft_entry__.build())")
+        # torch ships its own HIP runtime under the same soname; load it first
+        # so that libmak.so binds to the runtime that owns the device arena
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I32 = ctypes.c_void_p, ctypes.c_int32
         L.mak_plan.argtypes = [ctypes.POINTER(mak_config), ctypes.POINTER(ctypes.c_size_t)]
