@@ -29,6 +29,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_smollm2-135m.md")
+TRAFFIC_SOURCES = ["gemv_kernels.h", "device_math.h", "mak_internal.h", "gemv1_swiglu.hip", "gemv1_store.hip",
+                   "gemv1_residual.hip", "gemv1_logits.hip", "kernels.hip"]
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch of `kind` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE, calibrated against a copy of known
+    size), or None when the summary is for another kernel kind or the kernel
+    sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        line = line.strip()
+        for key in ("kernel_kind", "traffic_bytes_per_launch", "source_sha256"):
+            if line.startswith(key + ":"):
+                vals[key] = line.split(":", 1)[1].strip()
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "transformer_forward_pass_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("kernel_kind") != kind or vals.get("source_sha256") != h.hexdigest():
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 WORKLOAD = "smollm2-135m"
 SECONDARY = "llama-3.2-1b"
 
@@ -88,6 +116,9 @@ def measure(args, name, steps):
     """Throughput, token roofline and dominant-kernel roofline of one workload."""
     from transformer_forward_pass_amd import synth
     wl = synth.WORKLOADS[name]
+    if args.max_new:
+        import dataclasses
+        wl = dataclasses.replace(wl, max_new=args.max_new)
     shape = wl.shape
     w = synth.make_weights(shape)
     prompt = synth.make_prompts(wl)[0]
@@ -136,6 +167,8 @@ def main():
     ap.add_argument("--cpu-new", type=int, default=24, help="greedy tokens of the CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 1B-shape measurement")
+    ap.add_argument("--max-new", type=int, default=0,
+                    help="override the greedy token count (short counter-collection runs only)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -149,6 +182,7 @@ def main():
     r = measure(args, WORKLOAD, args.steps)
     wl = r["wl"]
     p0, n = len(r["prompt"]), wl.max_new
+    r["roofline"]["traffic"] = measured_traffic(r["roofline"]["kernel"])
     out = {
         "metric": "greedy decode tok/s at batch 1 (135M/1B shapes); % of HBM weight-streaming roofline",
         "value": round(r["tok_s"], 2),

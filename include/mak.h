@@ -153,9 +153,10 @@ int mak_set_executor(mak_model *m, int executor);
 
 /* Per-phase timing ("model-as-a-kernel", API: decode_step_timed runs the
  * phases one launch each and reports per-phase milliseconds).  While
- * enabled, every kernel the model launches is bracketed by hipEvents on the
- * model's stream and its duration is added to the total of its phase kind.
- * Enabling resets the totals.  mak_phase_times fills ms[MAK_PHASE_COUNT] and
+ * enabled, the phases run one launch each and every kernel carries a pair of
+ * hipEvents on the model's stream that HIP stamps at the kernel's own start
+ * and end; the duration is added to the total of its phase kind.  Enabling
+ * resets the totals.  mak_phase_times fills ms[MAK_PHASE_COUNT] and
  * launches[MAK_PHASE_COUNT] (either may be NULL). */
 #define MAK_PHASE_QKV 0    /* RMSNorm + Q/K/V GEMV                          */
 #define MAK_PHASE_ATTN 1   /* qk-norm, rope, KV append, attention           */

@@ -51,5 +51,30 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+MICRO = os.path.join(HERE, "microbench")
+MICRO_BIN = os.path.join(MICRO, "bin")
+
+
+def build_microbench(verbose: bool = False) -> None:
+    """Standalone measurement programs (sync_cost, mem_stream, copy_calib)."""
+    os.makedirs(MICRO_BIN, exist_ok=True)
+    srcs = sorted(f for f in os.listdir(MICRO) if f.endswith(".hip"))
+
+    def one(f):
+        out = os.path.join(MICRO_BIN, f[:-4])
+        cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=" + ARCH, "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+               "-o", out, os.path.join(MICRO, f)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (f, r.stderr))
+        return out
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        outs = list(ex.map(one, srcs))
+    if verbose:
+        print("built", " ".join(os.path.basename(o) for o in outs))
+
+
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_microbench(verbose=True)

@@ -14,6 +14,7 @@
 // row is reduced across the lanes that share it with a fixed xor tree.  No
 // floating-point atomics anywhere: the only atomic is the integer ticket that
 // elects the last workgroup of the LM head to finish the argmax.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -377,13 +378,21 @@ int mak_gemv_blocks(const GemvPhase& p, int cap)
     return std::max(1, (waves + wpb - 1) / wpb);
 }
 
-hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st)
+// Launch `fn`; with start/stop events, HIP stamps them at the kernel's own
+// begin and end (the dispatch packet's timestamps), not around the launch.
+static hipError_t launch_fn(const void* fn, dim3 grid, dim3 block, void** args, size_t lds, hipStream_t st,
+                            hipEvent_t e0, hipEvent_t e1)
 {
-    const void* fn = gemv_fn(p);
     if (!fn) return hipErrorInvalidValue;
+    if (e0 || e1) return hipExtLaunchKernel(fn, grid, block, args, lds, st, e0, e1, 0);
+    return hipLaunchKernel(fn, grid, block, args, lds, st);
+}
+
+hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
+{
     GemvPhase q = p;
     void* args[] = {&q};
-    return hipLaunchKernel(fn, dim3(p.n_blocks), dim3(MAK_BLOCK), args, gemv_lds(p), st);
+    return launch_fn(gemv_fn(p), dim3(p.n_blocks), dim3(MAK_BLOCK), args, gemv_lds(p), st, e0, e1);
 }
 
 // dynamic LDS of k_attn: pv[16][d] f64 | qf[d] f32 | kin, vin [8][d] bf16 |
@@ -402,29 +411,27 @@ size_t mak_attn_lds(const AttnPhase& p)
 
 #define MAK_ATTN_DIMS(X) X(32) X(64) X(128)
 
-hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st)
+hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const dim3 grid(p.ncols * p.n_q_heads), block(MAK_BLOCK);
-    const size_t lds = mak_attn_lds(p);
-#define X(D)                                                               \
-    if (p.head_dim == D) {                                                 \
-        hipLaunchKernelGGL((k_attn<D>), grid, block, lds, st, p);        \
-        return hipGetLastError();                                          \
-    }
+    const void* fn = reinterpret_cast<const void*>(&k_attn<0>);
+#define X(D) \
+    if (p.head_dim == D) fn = reinterpret_cast<const void*>(&k_attn<D>);
     MAK_ATTN_DIMS(X)
 #undef X
-    hipLaunchKernelGGL((k_attn<0>), grid, block, lds, st, p);
-    return hipGetLastError();
+    AttnPhase q = p;
+    void* args[] = {&q};
+    return launch_fn(fn, dim3(p.ncols * p.n_q_heads), dim3(MAK_BLOCK), args, mak_attn_lds(p), st, e0, e1);
 }
 
-hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st)
+hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st, hipEvent_t e0,
+                              hipEvent_t e1)
 {
     CtlInit in = {};
     for (int c = 0; c < ncols && c < MAK_MAX_COLS; c++) in.cols[c] = cols[c];
     in.ncols = ncols;
     in.step = step;
-    hipLaunchKernelGGL(k_set_ctl, dim3(1), dim3(64), 0, st, ctl, in);
-    return hipGetLastError();
+    void* args[] = {&ctl, &in};
+    return launch_fn(reinterpret_cast<const void*>(&k_set_ctl), dim3(1), dim3(64), args, 0, st, e0, e1);
 }
 
 // Raise the dynamic-LDS ceiling of the GEMV instantiations to `bytes` and of

@@ -22,9 +22,10 @@
 #include "mak_internal.h"
 
 // kernels.hip
-hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st);
-hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st);
-hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st);
+hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st, hipEvent_t e0,
+                              hipEvent_t e1);
 hipError_t mak_set_lds_limit(int bytes, int attn_bytes);
 size_t mak_attn_lds_for(int rep, int d, int max_seq);
 size_t mak_attn_lds(const AttnPhase& p);
@@ -291,8 +292,8 @@ hipEvent_t take_event(mak_model* m)
     return e;
 }
 
-// Launch through `fn` (returns hipError_t); with phase timing on, bracket
-// the launch with events on the model's stream.
+// Launch through `fn(e0, e1)` (returns hipError_t).  With phase timing on,
+// e0/e1 are events that HIP stamps at the kernel's own start and end.
 template <class F>
 int launch(mak_model* m, int kind, F&& fn)
 {
@@ -301,13 +302,9 @@ int launch(mak_model* m, int kind, F&& fn)
         a = take_event(m);
         b = take_event(m);
         if (!a || !b) return fail(MAK_EDEVICE, "hipEventCreate failed");
-        HIP_TRY(hipEventRecord(a, m->cur));
     }
-    HIP_TRY(fn());
-    if (m->tm.on) {
-        HIP_TRY(hipEventRecord(b, m->cur));
-        m->tm.pending.push_back({a, b, kind});
-    }
+    HIP_TRY(fn(a, b));
+    if (m->tm.on) m->tm.pending.push_back({a, b, kind});
     return MAK_OK;
 }
 
@@ -354,7 +351,7 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
             (size_t)mak_gemv_nc(q.ncols) * q.geo.k * 2 > (size_t)kLdsBudget ||
             (q.epi == EPI_SWIGLU && (q.geo.r % 2)))
             return fail(MAK_EINVAL, "internal: bad GEMV phase");
-        int rc = launch(m, kind, [&] { return mak_launch_gemv(q, m->cur); });
+        int rc = launch(m, kind, [&](hipEvent_t e0, hipEvent_t e1) { return mak_launch_gemv(q, m->cur, e0, e1); });
         if (rc) return rc;
     }
     return MAK_OK;
@@ -416,7 +413,10 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
         a.eps = c.rms_eps;
         a.scale = (float)(1.0 / std::sqrt((double)d));
         if (mak_attn_lds(a) > (size_t)kAttnLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
-        if ((rc = launch(m, MAK_PHASE_ATTN, [&] { return mak_launch_attn(a, m->cur); }))) return rc;
+        if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
+                 return mak_launch_attn(a, m->cur, e0, e1);
+             })))
+            return rc;
 
         // O + residual
         GemvPhase po{};
@@ -524,7 +524,9 @@ int set_cols(mak_model* m, const ColState* cols, int ncols, int step)
 {
     m->cur = m->stream;
     return launch(m, MAK_PHASE_CTL,
-                  [&] { return mak_launch_set_ctl(m->at<Ctl>(m->L.ctl), cols, ncols, step, m->stream); });
+                  [&](hipEvent_t e0, hipEvent_t e1) {
+                      return mak_launch_set_ctl(m->at<Ctl>(m->L.ctl), cols, ncols, step, m->stream, e0, e1);
+                  });
 }
 
 // Consume ids[0..n) of `slot` from start_pos; LM head on the last token when
