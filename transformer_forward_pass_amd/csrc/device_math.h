@@ -86,6 +86,43 @@ __device__ __forceinline__ double group_sum_rt(double v, int log)
     return v;
 }
 
+// group_sum_rt over N values at once, level by level, so the cross-lane
+// moves of different values overlap instead of waiting on each other.
+template <int N>
+__device__ __forceinline__ void group_sum_all(double (&v)[N], int log)
+{
+    if (log >= 1) {
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] += dpp_d<DPP_XOR1>(v[i]);
+    }
+    if (log >= 2) {
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] += dpp_d<DPP_XOR2>(v[i]);
+    }
+    if (log >= 3) {
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] += dpp_d<DPP_HALF_MIRROR>(v[i]);
+    }
+    if (log >= 4) {
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] += dpp_d<DPP_MIRROR>(v[i]);
+    }
+    if (log >= 5) {
+        double t[N];
+#pragma unroll
+        for (int i = 0; i < N; i++) t[i] = __shfl_xor(v[i], 16, 64);
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] += t[i];
+    }
+    if (log >= 6) {
+        double t[N];
+#pragma unroll
+        for (int i = 0; i < N; i++) t[i] = __shfl_xor(v[i], 32, 64);
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] += t[i];
+    }
+}
+
 template <int LOG>
 __device__ __forceinline__ float group_max(float v)
 {
@@ -128,6 +165,34 @@ __device__ __forceinline__ double block_sum(double v, double* red)
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
     double s = ((red[0] + red[1]) + red[2]) + red[3];
+    return s;
+}
+
+// Block-wide fp64 sum over NW waves, combined in wave order.
+template <int NW>
+__device__ __forceinline__ double block_sum_n(double v, double* red)
+{
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; i++) s += red[i];
+    return s;
+}
+
+// Block-wide fp64 sum over nw waves (runtime), combined in wave order.
+__device__ __forceinline__ double block_sum_rt(double v, double* red, int nw)
+{
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = red[0];
+    for (int i = 1; i < nw; i++) s += red[i];
     return s;
 }
 

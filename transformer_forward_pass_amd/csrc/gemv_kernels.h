@@ -47,7 +47,7 @@ struct Staged {
 };
 
 template <int NC>
-__device__ __forceinline__ void issue_input(const GemvPhase& p, Staged<NC>& st)
+__device__ __forceinline__ void issue_input(const GemvPhase& p, Staged<NC>& st, const int NT)
 {
     constexpr int QPT = Staged<NC>::QPT;
     const int C = p.geo.k >> 3;
@@ -64,7 +64,7 @@ __device__ __forceinline__ void issue_input(const GemvPhase& p, Staged<NC>& st)
     }
 #pragma unroll
     for (int i = 0; i < QPT; i++) {
-        const int q = tid + i * MAK_BLOCK;
+        const int q = tid + i * NT;
 #pragma unroll
         for (int c = 0; c < NC; c++) {
             if (q < C && src[c]) {
@@ -79,7 +79,8 @@ __device__ __forceinline__ void issue_input(const GemvPhase& p, Staged<NC>& st)
 }
 
 template <int NC>
-__device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st, uint16_t* hs, double* red)
+__device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st, uint16_t* hs, double* red,
+                                             const int NT)
 {
     constexpr int QPT = Staged<NC>::QPT;
     const int K = p.geo.k, C = K >> 3;
@@ -89,25 +90,25 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
         uint4* h4 = reinterpret_cast<uint4*>(hs + (size_t)c * K);
         const int col = p.col0 + c;
         if (c >= p.ncols) {
-            for (int q = tid; q < C; q += MAK_BLOCK) h4[q] = make_uint4(0, 0, 0, 0);
+            for (int q = tid; q < C; q += NT) h4[q] = make_uint4(0, 0, 0, 0);
             continue;
         }
         if (p.in_kind == IN_RAW) {
 #pragma unroll
             for (int i = 0; i < QPT; i++) {
-                const int q = tid + i * MAK_BLOCK;
+                const int q = tid + i * NT;
                 if (q < C) h4[q] = st.v[c][i];
             }
             // chunks beyond what the registers held (K > QPT*2048)
             const uint4* src = reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
-            for (int q = tid + QPT * MAK_BLOCK; q < C; q += MAK_BLOCK) h4[q] = src[q];
+            for (int q = tid + QPT * NT; q < C; q += NT) h4[q] = src[q];
             continue;
         }
         // RMSNorm of x (K <= 4096: at most 2 chunks per thread)
         double ss = 0.0;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            const int q = tid + i * MAK_BLOCK;
+            const int q = tid + i * NT;
             if (q < C) {
                 if (p.in_kind == IN_GATHER_NORM && blockIdx.x == 0)
                     reinterpret_cast<uint4*>(p.x_store + (size_t)col * p.x_ld)[q] = st.v[c][i];
@@ -120,11 +121,11 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
                 }
             }
         }
-        ss = block_sum(ss, red);
+        ss = block_sum_rt(ss, red, NT >> 6);
         const float r = rms_scale(ss, K, p.eps);
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            const int q = tid + i * MAK_BLOCK;
+            const int q = tid + i * NT;
             if (q < C) {
                 const uint32_t u[4] = {st.v[c][i].x, st.v[c][i].y, st.v[c][i].z, st.v[c][i].w};
                 const uint32_t ww[4] = {st.w[i].x, st.w[i].y, st.w[i].z, st.w[i].w};
@@ -149,9 +150,10 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
 // index), then the last block to finish (integer ticket) reduces every
 // block's partial and feeds the chosen tokens back as the next step's columns.
 template <int NC>
-__device__ void argmax_tail(const GemvPhase& p, const float* best_v, const int* best_i, float (*bval)[NC],
-                            int (*bidx)[NC], int& is_last, int lane, int wave)
+__device__ __forceinline__ void argmax_tail(const GemvPhase& p, const float* best_v, const int* best_i, float (*bval)[NC],
+                            int (*bidx)[NC], int& is_last, int lane, int wave, const int NW)
 {
+    const int NT = NW * 64;
     // ---- greedy argmax: per-block partial, then the last block reduces ----
 #pragma unroll
     for (int c = 0; c < NC; c++) {
@@ -175,7 +177,7 @@ __device__ void argmax_tail(const GemvPhase& p, const float* best_v, const int* 
         const int c = threadIdx.x;
         float v = bval[0][c];
         int i = bidx[0][c];
-        for (int w = 1; w < 4; w++) {
+        for (int w = 1; w < NW; w++) {
             if (bval[w][c] > v || (bval[w][c] == v && bidx[w][c] < i)) {
                 v = bval[w][c];
                 i = bidx[w][c];
@@ -195,12 +197,13 @@ __device__ void argmax_tail(const GemvPhase& p, const float* best_v, const int* 
     __threadfence();
 
     // the last block: reduce every block's partial (order-free: max, then
-    // lowest index), then feed the chosen tokens back as the next step's columns
+    // lowest index), one wave per column, then feed the chosen tokens back as
+    // the next step's columns
     __shared__ int next_tok[MAK_MAX_COLS];
-    for (int c = 0; c < p.ncols; c++) {
+    for (int c = wave; c < p.ncols; c += NW) {
         float v = -INFINITY;
         int i = 0x7fffffff;
-        for (int b = threadIdx.x; b < p.n_blocks; b += MAK_BLOCK) {
+        for (int b = lane; b < p.n_blocks; b += 64) {
             const float v2 = p.part_val[b * MAK_MAX_COLS + c];
             const int i2 = p.part_idx[b * MAK_MAX_COLS + c];
             if (v2 > v || (v2 == v && i2 < i)) {
@@ -216,22 +219,9 @@ __device__ void argmax_tail(const GemvPhase& p, const float* best_v, const int* 
                 i = i2;
             }
         }
-        if (lane == 0) {
-            bval[wave][0] = v;
-            bidx[wave][0] = i;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int w = 1; w < 4; w++) {
-                if (bval[w][0] > v || (bval[w][0] == v && bidx[w][0] < i)) {
-                    v = bval[w][0];
-                    i = bidx[w][0];
-                }
-            }
-            next_tok[c] = (i == 0x7fffffff) ? 0 : i;
-        }
-        __syncthreads();
+        if (lane == 0) next_tok[c] = (i == 0x7fffffff) ? 0 : i;
     }
+    __syncthreads();
     if (threadIdx.x == 0) {
         // new column c takes over from column col0 + c >= c, so updating in
         // ascending order never overwrites a column still to be read
@@ -270,12 +260,13 @@ __device__ __forceinline__ void batch_ready(const uint4 (&b)[QB], int n)
 }
 
 template <int R, int NC, int EPI>
-__global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
+__global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ double red[4];
-    __shared__ float bval[4][NC];
-    __shared__ int bidx[4][NC];
+    constexpr int NW = MAK_GBLOCK / 64;
+    __shared__ double red[NW];
+    __shared__ float bval[NW][NC];
+    __shared__ int bidx[NW][NC];
     __shared__ int is_last;
     uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
 
@@ -292,7 +283,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
     const int J = (K >> 3) >> lrl;
     const int Q = J * R;                       // 16-byte loads per lane per tile
     const uint4* W = reinterpret_cast<const uint4*>(p.w);
-    const int n_waves = gridDim.x * (MAK_BLOCK / 64);
+    const int n_waves = gridDim.x * (MAK_GBLOCK / 64);
     const int N = p.geo.n_rows;
     constexpr int QB = (NC <= 2) ? 16 : 8;     // loads per batch (a multiple of R)
     static_assert(QB % R == 0, "batch must hold whole row groups");
@@ -310,12 +301,12 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
             if (i < n) buf[i] = *reinterpret_cast<const uint4*>(wt + (lane_off + (uint32_t)i * 1024u));
     };
 
-    int tile = blockIdx.x * (MAK_BLOCK / 64) + wave;
+    int tile = blockIdx.x * (MAK_GBLOCK / 64) + wave;
 
     // 1. this step's input, the residual rows of the first tile (lane s == 0
     //    owns rows row0 .. row0+R-1), then the first weight batch
     Staged<NC> stg;
-    issue_input<NC>(p, stg);
+    issue_input<NC>(p, stg, MAK_GBLOCK);
     float xres[R][NC];
     auto load_res = [&](int t) {
         if (EPI == EPI_RESIDUAL && s == 0) {
@@ -336,7 +327,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
     }
 
     // 2. stage the input (RMSNorm); this waits for the first batch as well
-    finish_input<NC>(p, stg, hs, red);
+    finish_input<NC>(p, stg, hs, red, MAK_GBLOCK);
     __syncthreads();
 
     float best_v[NC];
@@ -492,7 +483,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
         b = nbt;
     }
 
-    if (EPI == EPI_LOGITS) argmax_tail<NC>(p, best_v, best_i, bval, bidx, is_last, lane, wave);
+    if (EPI == EPI_LOGITS) argmax_tail<NC>(p, best_v, best_i, bval, bidx, is_last, lane, wave, NW);
 }
 
 // ---------------------------------------------------------------------------
@@ -502,14 +493,20 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv(GemvPhase p)
 // the next tile's batch is issued and only then is the current one folded, so
 // the stream never stops while the wave computes.
 // ---------------------------------------------------------------------------
+// Waves per workgroup of k_gemv1<R, J>: 8, or 4 where two batch buffers of
+// J*R loads need more registers than two waves per SIMD leave.
+__host__ __device__ constexpr int gemv1_waves(int r, int j) { return r * j > 16 ? 4 : 8; }
+
 template <int R, int J, int EPI>
-__global__ __launch_bounds__(MAK_BLOCK) void k_gemv1(GemvPhase p)
+__global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
 {
     constexpr int QT = J * R;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ double red[4];
-    __shared__ float bval[4][1];
-    __shared__ int bidx[4][1];
+    constexpr int NW = gemv1_waves(R, J);
+    __shared__ double red[NW];
+    __shared__ float bval[NW][1];
+    __shared__ int bidx[NW][1];
+    __shared__ int tile_next;
     __shared__ int is_last;
     uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
 
@@ -522,7 +519,8 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv1(GemvPhase p)
     const int G = 64 >> lrl;
     const int n_tiles = p.geo.n_tiles;
     const int N = p.geo.n_rows;
-    const int n_waves = gridDim.x * (MAK_BLOCK / 64);
+    const int nw = blockDim.x >> 6;                        // <= NW (one tile per wave: 4)
+    const int n_waves = gridDim.x * nw;
     const char* W = reinterpret_cast<const char*>(p.w);
     const uint32_t lane_off = (uint32_t)lane * 16u;
 
@@ -532,9 +530,24 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv1(GemvPhase p)
         for (int i = 0; i < QT; i++) buf[i] = *reinterpret_cast<const uint4*>(wt + lane_off + i * 1024);
     };
 
-    int tile = blockIdx.x * (MAK_BLOCK / 64) + wave;
+    // Tiles.  With at most one tile per wave: tile = global wave index.
+    // Otherwise each workgroup owns a contiguous range of tiles and its waves
+    // take them one at a time from an LDS counter, so waves that get more
+    // of the CU's memory bandwidth do more tiles and all finish together
+    // (which tile a wave computes does not change any result).
+    const bool dyn = n_tiles > n_waves;
+    const int t_begin = dyn ? (int)((int64_t)blockIdx.x * n_tiles / gridDim.x) : 0;
+    const int t_end = dyn ? (int)((int64_t)(blockIdx.x + 1) * n_tiles / gridDim.x) : n_tiles;
+    int tile = dyn ? t_begin + wave : blockIdx.x * nw + wave;   // dyn: each range holds >= nw tiles
+    if (threadIdx.x == 0) tile_next = t_begin + nw;
+    auto next_tile = [&](int t) __attribute__((always_inline)) {
+        if (!dyn) return t + n_waves;
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&tile_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
     Staged<1> stg;
-    issue_input<1>(p, stg);
+    issue_input<1>(p, stg, nw * 64);
     float xres[R];
     auto load_res = [&](int t) {
         if (EPI == EPI_RESIDUAL && s == 0) {
@@ -545,18 +558,14 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv1(GemvPhase p)
         }
     };
     uint4 bufA[QT], bufB[QT];
-    // A wave with a single tile issues it before staging the input: both
-    // arrive in one round trip.  With several tiles per wave the chip-wide
-    // first batch is large, so the input (RMSNorm) is staged first and the
-    // stream starts right after it.
-    const bool weights_first = n_tiles <= n_waves;
-    if (tile < n_tiles) {
+    // the first weight batch is issued before the input is staged, so both
+    // arrive in one round trip and the stream starts at once
+    if (tile < t_end) {
         load_res(tile);
-        if (weights_first) issue(bufA, tile);
+        issue(bufA, tile);
     }
-    finish_input<1>(p, stg, hs, red);
-    __syncthreads();
-    if (!weights_first && tile < n_tiles) issue(bufA, tile);
+    finish_input<1>(p, stg, hs, red, nw * 64);
+    __syncthreads();   // also publishes tile_next
 
     float best_v = -INFINITY;
     int best_i = 0x7fffffff;
@@ -629,22 +638,22 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv1(GemvPhase p)
         }
     };
 
-    while (tile < n_tiles) {
-        int nt = tile + n_waves;
+    while (tile < t_end) {
+        int nt = next_tile(tile);
         batch_ready<QT>(bufA, QT);
-        if (nt < n_tiles) issue(bufB, nt);
+        if (nt < t_end) issue(bufB, nt);
         fold(bufA, tile);
-        if (nt < n_tiles) load_res(nt);
+        if (nt < t_end) load_res(nt);
         tile = nt;
-        if (tile >= n_tiles) break;
-        nt = tile + n_waves;
+        if (tile >= t_end) break;
+        nt = next_tile(tile);
         batch_ready<QT>(bufB, QT);
-        if (nt < n_tiles) issue(bufA, nt);
+        if (nt < t_end) issue(bufA, nt);
         fold(bufB, tile);
-        if (nt < n_tiles) load_res(nt);
+        if (nt < t_end) load_res(nt);
         tile = nt;
     }
-    if (EPI == EPI_LOGITS) argmax_tail<1>(p, &best_v, &best_i, bval, bidx, is_last, lane, wave);
+    if (EPI == EPI_LOGITS) argmax_tail<1>(p, &best_v, &best_i, bval, bidx, is_last, lane, wave, nw);
 }
 
 }  // namespace mak

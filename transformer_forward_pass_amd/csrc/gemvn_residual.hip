@@ -1,0 +1,13 @@
+// gemvn_residual.hip -- multi-column GEMV instantiations, residual-add epilogue.
+#include "gemvn_kernels.h"
+
+using namespace mak;
+
+const void* mak_gemvn_fn_residual(int rr, int nc)
+{
+#define X(RR, NC) \
+    if (rr == RR && nc == NC) return reinterpret_cast<const void*>(&k_gemvn<RR, NC, EPI_RESIDUAL>);
+    MAK_GEMVN_SHAPES(X)
+#undef X
+    return nullptr;
+}

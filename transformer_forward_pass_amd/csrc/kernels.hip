@@ -25,6 +25,7 @@
 #include "mak_internal.h"
 
 #include "gemv_kernels.h"
+#include "gemvn_kernels.h"
 
 namespace mak {
 
@@ -282,26 +283,15 @@ __global__ void k_set_ctl(Ctl* ctl, CtlInit in)
 // ---------------------------------------------------------------------------
 using namespace mak;
 
-template <int R, int NC>
-static const void* gemv_fn_rn(int epi)
+// batch-1 GEMV for tile shapes without a compiled k_gemv1
+template <int R>
+static const void* gemv_fn_r1(int epi)
 {
     switch (epi) {
-    case EPI_STORE: return reinterpret_cast<const void*>(&k_gemv<R, NC, EPI_STORE>);
-    case EPI_RESIDUAL: return reinterpret_cast<const void*>(&k_gemv<R, NC, EPI_RESIDUAL>);
-    case EPI_SWIGLU: return reinterpret_cast<const void*>(&k_gemv<R, NC, EPI_SWIGLU>);
-    case EPI_LOGITS: return reinterpret_cast<const void*>(&k_gemv<R, NC, EPI_LOGITS>);
-    }
-    return nullptr;
-}
-
-template <int R>
-static const void* gemv_fn_r(int nc, int epi)
-{
-    switch (nc) {
-    case 1: return gemv_fn_rn<R, 1>(epi);
-    case 2: return gemv_fn_rn<R, 2>(epi);
-    case 4: return gemv_fn_rn<R, 4>(epi);
-    case 8: return gemv_fn_rn<R, 8>(epi);
+    case EPI_STORE: return reinterpret_cast<const void*>(&k_gemv<R, 1, EPI_STORE>);
+    case EPI_RESIDUAL: return reinterpret_cast<const void*>(&k_gemv<R, 1, EPI_RESIDUAL>);
+    case EPI_SWIGLU: return reinterpret_cast<const void*>(&k_gemv<R, 1, EPI_SWIGLU>);
+    case EPI_LOGITS: return reinterpret_cast<const void*>(&k_gemv<R, 1, EPI_LOGITS>);
     }
     return nullptr;
 }
@@ -309,34 +299,52 @@ static const void* gemv_fn_r(int nc, int epi)
 // Column capacity (template NC) for n active columns.
 int mak_gemv_nc(int ncols) { return ncols <= 1 ? 1 : ncols <= 2 ? 2 : ncols <= 4 ? 4 : 8; }
 
-static const void* gemv_fn(const GemvPhase& p)
+static const void* gemvn_fn(int rr, int nc, int epi)
 {
-    if (p.ncols == 1) {
-        const int j = (p.geo.k >> 3) >> p.geo.lr_log2;
-        const void* f = nullptr;
-        switch (p.epi) {
-        case EPI_STORE: f = mak_gemv1_fn_store(p.geo.r, j); break;
-        case EPI_RESIDUAL: f = mak_gemv1_fn_residual(p.geo.r, j); break;
-        case EPI_SWIGLU: f = mak_gemv1_fn_swiglu(p.geo.r, j); break;
-        case EPI_LOGITS: f = mak_gemv1_fn_logits(p.geo.r, j); break;
-        }
-        if (f) return f;
-    }
-    const int nc = mak_gemv_nc(p.ncols);
-    switch (p.geo.r) {
-    case 1: return gemv_fn_r<1>(nc, p.epi);
-    case 2: return gemv_fn_r<2>(nc, p.epi);
-    case 4: return gemv_fn_r<4>(nc, p.epi);
+    switch (epi) {
+    case EPI_STORE: return mak_gemvn_fn_store(rr, nc);
+    case EPI_RESIDUAL: return mak_gemvn_fn_residual(rr, nc);
+    case EPI_SWIGLU: return mak_gemvn_fn_swiglu(rr, nc);
+    case EPI_LOGITS: return mak_gemvn_fn_logits(rr, nc);
     }
     return nullptr;
 }
 
-static size_t gemv_lds(const GemvPhase& p) { return (size_t)mak_gemv_nc(p.ncols) * p.geo.k * sizeof(uint16_t); }
+static const void* gemv1_fn(const GemvPhase& p)
+{
+    const int j = (p.geo.k >> 3) >> p.geo.lr_log2;
+    switch (p.epi) {
+    case EPI_STORE: return mak_gemv1_fn_store(p.geo.r, j);
+    case EPI_RESIDUAL: return mak_gemv1_fn_residual(p.geo.r, j);
+    case EPI_SWIGLU: return mak_gemv1_fn_swiglu(p.geo.r, j);
+    case EPI_LOGITS: return mak_gemv1_fn_logits(p.geo.r, j);
+    }
+    return nullptr;
+}
 
-// Grid of a GEMV phase: one wave per tile while that fits on the chip at
-// once; otherwise the resident capacity (occupancy x CUs), with the tiles
-// spread evenly so that every wave streams the same number of tiles.
-int mak_gemv_blocks(const GemvPhase& p, int cap)
+static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn(p) != nullptr; }
+
+static const void* gemv_fn(const GemvPhase& p)
+{
+    if (p.ncols >= 2) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
+    if (const void* f = gemv1_fn(p)) return f;
+    switch (p.geo.r) {
+    case 1: return gemv_fn_r1<1>(p.epi);
+    case 2: return gemv_fn_r1<2>(p.epi);
+    case 4: return gemv_fn_r1<4>(p.epi);
+    }
+    return nullptr;
+}
+
+static int gemv_threads(const GemvPhase& p) { return p.threads; }
+
+size_t mak_gemv_lds(const GemvPhase& p)
+{
+    if (p.ncols >= 2) return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.geo.lr_log2);
+    return (size_t)p.geo.k * sizeof(uint16_t);
+}
+
+static int device_cus()
 {
     static int n_cu = 0;
     if (!n_cu) {
@@ -345,37 +353,95 @@ int mak_gemv_blocks(const GemvPhase& p, int cap)
             hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
             n_cu = 256;
     }
-    // resident blocks per CU of this instantiation (cached per kernel and LDS size)
+    return n_cu;
+}
+
+// resident workgroups per CU of `fn` with `lds` bytes of dynamic LDS (cached)
+static int resident_blocks(const void* fn, int threads, size_t lds)
+{
     struct OccEntry {
         const void* fn;
         size_t lds;
         int occ;
     };
-    static OccEntry cache[128];
+    static OccEntry cache[256];
     static int n_cache = 0;
-    const void* fn = gemv_fn(p);
-    const size_t lds = gemv_lds(p);
-    int occ = 0;
     for (int i = 0; i < n_cache; i++)
-        if (cache[i].fn == fn && cache[i].lds == lds) occ = cache[i].occ;
-    if (!occ) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, MAK_BLOCK, lds) != hipSuccess || occ <= 0)
-            occ = 1;
-        if (n_cache < 128) cache[n_cache++] = {fn, lds, occ};
+        if (cache[i].fn == fn && cache[i].lds == lds) return cache[i].occ;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, threads, lds) != hipSuccess || occ <= 0) occ = 1;
+    if (n_cache < 256) cache[n_cache++] = {fn, lds, occ};
+    return occ;
+}
+
+// Multi-column work split: rows per lane rr (as many as keep >= 1024 tile
+// groups and fit the LDS budget), then waves per group jw (a power of two <=
+// the chunk iterations) until about 2048 waves are busy.
+static void gemvn_plan(GemvPhase& p, size_t lds_budget)
+{
+    const int nc = mak_gemv_nc(p.ncols);
+    const int R = p.geo.r, lrl = p.geo.lr_log2;
+    const int J = (p.geo.k >> 3) >> lrl;
+    const int64_t tiles = p.geo.n_tiles;
+    int rr = R;
+    for (int cand : {4, 2}) {
+        if (cand < R || cand % R) continue;
+        if ((tiles + cand / R - 1) / (cand / R) >= 1024 && gemvn_lds(nc, p.geo.k, cand, lrl) <= lds_budget) {
+            rr = cand;
+            break;
+        }
     }
-    // optional cap on resident blocks per CU (tuning knob for large matrices)
-    static int per_cu_cap = -1;
-    if (per_cu_cap < 0) {
+    const int64_t ng = (tiles + rr / R - 1) / (rr / R);
+    int jw = 1;
+    while (jw * 2 <= MAK_NBLOCK / 64 && jw * 2 <= J && ng * jw < 2048) jw *= 2;
+    p.rr = rr;
+    p.jw = jw;
+}
+
+// Grid of a GEMV phase.  Batch-1: one wave per tile while that fits on the
+// chip at once; otherwise the resident capacity (occupancy x CUs), with the
+// tiles spread evenly so that every wave streams the same number of tiles.
+// Multi-column: the work split of gemvn_plan, one workgroup per group slot
+// up to the resident capacity.
+int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
+{
+    const int n_cu = device_cus();
+    if (p.ncols >= 2) {
+        gemvn_plan(p, lds_budget_n);
+        p.threads = MAK_NBLOCK;
+        const void* fn = gemv_fn(p);
+        if (!fn) return 0;
+        const int occ = resident_blocks(fn, MAK_NBLOCK, mak_gemv_lds(p));
+        const int64_t ng = (p.geo.n_tiles + p.rr / p.geo.r - 1) / (p.rr / p.geo.r);
+        const int64_t gpr = (MAK_NBLOCK / 64) / p.jw;
+        const int64_t want = (ng + gpr - 1) / gpr;
+        return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min(occ * n_cu, cap)));
+    }
+    const void* fn = gemv_fn(p);
+    if (!fn) return 0;
+    // batch-1: one tile per wave in workgroups of 4 waves while that keeps
+    // <= 8 waves per CU; beyond, one workgroup per CU (8 waves, or 4 for
+    // shapes whose batch buffers need the registers of two waves) whose
+    // waves share its tile range (k_gemv1 hands the tiles out dynamically,
+    // k_gemv strides over them)
+    static int per_cu = -1;   // optional override of workgroups per CU (tuning knob)
+    if (per_cu < 0) {
         const char* e = getenv("MAK_GEMV_BLOCKS_PER_CU");
-        per_cu_cap = (e && atoi(e) > 0) ? atoi(e) : 0;
+        per_cu = (e && atoi(e) > 0) ? atoi(e) : 1;
     }
-    if (per_cu_cap > 0) occ = std::min(occ, per_cu_cap);
-    const int wpb = MAK_BLOCK / 64;
-    const int max_waves = std::min(occ * n_cu, cap) * wpb;
-    const int tiles = p.geo.n_tiles;
-    const int per_wave = (tiles + max_waves - 1) / max_waves;
-    const int waves = (tiles + per_wave - 1) / per_wave;
-    return std::max(1, (waves + wpb - 1) / wpb);
+    const int64_t tiles = p.geo.n_tiles;
+    if (!gemv1_compiled(p)) {
+        p.threads = MAK_GBLOCK;
+        const int wpb = MAK_GBLOCK / 64;
+        return (int)std::max<int64_t>(1, std::min<int64_t>((tiles + wpb - 1) / wpb, std::min(per_cu * n_cu, cap)));
+    }
+    if (tiles <= 8 * (int64_t)n_cu) {
+        p.threads = 256;
+        return (int)std::min<int64_t>((tiles + 3) / 4, cap);
+    }
+    const int j = (p.geo.k >> 3) >> p.geo.lr_log2;
+    p.threads = gemv1_waves(p.geo.r, j) * 64;
+    return (int)std::max(1, std::min(per_cu * n_cu, cap));
 }
 
 // Launch `fn`; with start/stop events, HIP stamps them at the kernel's own
@@ -392,7 +458,7 @@ hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hi
 {
     GemvPhase q = p;
     void* args[] = {&q};
-    return launch_fn(gemv_fn(p), dim3(p.n_blocks), dim3(MAK_BLOCK), args, gemv_lds(p), st, e0, e1);
+    return launch_fn(gemv_fn(p), dim3(p.n_blocks), dim3(gemv_threads(p)), args, mak_gemv_lds(p), st, e0, e1);
 }
 
 // dynamic LDS of k_attn: pv[16][d] f64 | qf[d] f32 | kin, vin [8][d] bf16 |
@@ -434,29 +500,31 @@ hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int ste
     return launch_fn(reinterpret_cast<const void*>(&k_set_ctl), dim3(1), dim3(64), args, 0, st, e0, e1);
 }
 
-// Raise the dynamic-LDS ceiling of the GEMV instantiations to `bytes` and of
-// the attention kernel to `attn_bytes`.
-hipError_t mak_set_lds_limit(int bytes, int attn_bytes)
+// Raise the dynamic-LDS ceiling of the batch-1 GEMV instantiations to
+// `bytes`, of the multi-column ones to `bytes_n` and of the attention kernel
+// to `attn_bytes`.
+hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
 {
-#define SETA(R, NC, E)                                                                          \
-    do {                                                                                        \
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<R, NC, E>),    \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);  \
-        if (e != hipSuccess) return e;                                                          \
-    } while (0)
-#define SETE(R, NC) SETA(R, NC, EPI_STORE); SETA(R, NC, EPI_RESIDUAL); SETA(R, NC, EPI_SWIGLU); SETA(R, NC, EPI_LOGITS)
-#define SETN(R) SETE(R, 1); SETE(R, 2); SETE(R, 4); SETE(R, 8)
-    SETN(1);
-    SETN(2);
-    SETN(4);
+    auto set = [](const void* f, int b) {
+        return f ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, b) : hipSuccess;
+    };
+    for (int r : {1, 2, 4})
+        for (int epi : {(int)EPI_STORE, (int)EPI_RESIDUAL, (int)EPI_SWIGLU, (int)EPI_LOGITS}) {
+            const void* f = (r == 1) ? gemv_fn_r1<1>(epi) : (r == 2) ? gemv_fn_r1<2>(epi) : gemv_fn_r1<4>(epi);
+            hipError_t e = set(f, bytes);
+            if (e != hipSuccess) return e;
+            for (int nc : {2, 4, 8}) {
+                e = set(gemvn_fn(r, nc, epi), bytes_n);
+                if (e != hipSuccess) return e;
+            }
+        }
     for (int r : {1, 2, 4})
         for (int j : {1, 2, 3, 4, 6, 9, 11, 16})
             for (const void* f : {mak_gemv1_fn_store(r, j), mak_gemv1_fn_residual(r, j), mak_gemv1_fn_swiglu(r, j),
-                                  mak_gemv1_fn_logits(r, j)})
-                if (f) {
-                    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-                    if (e != hipSuccess) return e;
-                }
+                                  mak_gemv1_fn_logits(r, j)}) {
+                hipError_t e = set(f, bytes);
+                if (e != hipSuccess) return e;
+            }
 #define X(D)                                                                               \
     {                                                                                      \
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D>),       \
@@ -468,7 +536,4 @@ hipError_t mak_set_lds_limit(int bytes, int attn_bytes)
 #undef X
     return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<0>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, attn_bytes);
-#undef SETA
-#undef SETE
-#undef SETN
 }

@@ -26,11 +26,12 @@ hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hi
 hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st, hipEvent_t e0,
                               hipEvent_t e1);
-hipError_t mak_set_lds_limit(int bytes, int attn_bytes);
+hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes);
 size_t mak_attn_lds_for(int rep, int d, int max_seq);
 size_t mak_attn_lds(const AttnPhase& p);
 int mak_gemv_nc(int ncols);
-int mak_gemv_blocks(const GemvPhase& p, int cap);
+int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n);
+size_t mak_gemv_lds(const GemvPhase& p);
 
 namespace {
 
@@ -56,7 +57,9 @@ int fail(int code, const char* fmt, ...)
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxGemvBlocks = 1024;      // grid cap of a GEMV phase (waves loop over tiles)
-constexpr int kLdsBudget = 60 * 1024;      // GEMV dynamic LDS per workgroup (static LDS < 4 KiB)
+constexpr int kLdsBudget = 60 * 1024;      // batch-1 GEMV dynamic LDS per workgroup (static LDS < 4 KiB)
+constexpr int kLdsBudgetN = 144 * 1024;    // multi-column GEMV: staged inputs (<= 128 KiB) + partial sums
+constexpr int kLdsInputsN = 128 * 1024;    // multi-column GEMV: NC input rows of K bf16
 constexpr int kAttnLdsBudget = 150 * 1024; // attention dynamic LDS (gfx950: 160 KiB per workgroup)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -326,7 +329,7 @@ int collect_timing(mak_model* m)
 // Largest column group whose bf16 input rows fit the LDS budget.
 int max_cols_for_k(int k)
 {
-    int n = kLdsBudget / (k * 2);
+    int n = kLdsInputsN / (k * 2);
     if (n >= 8) return 8;
     if (n >= 4) return 4;
     if (n >= 2) return 2;
@@ -343,13 +346,14 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
         GemvPhase q = p;
         q.col0 = col0 + c0;
         q.ncols = std::min(step, ncols - c0);
-        q.n_blocks = mak_gemv_blocks(q, kMaxGemvBlocks);
+        q.n_blocks = mak_gemv_blocks(q, kMaxGemvBlocks, kLdsBudgetN);
         if (q.epi == EPI_LOGITS && q.col0 != col0)
             return fail(MAK_EINVAL, "internal: LM head split");
         // host-side shape checks of what the kernel assumes
         if (q.geo.k % 8 || q.ncols < 1 || q.ncols > MAK_MAX_COLS || q.col0 + q.ncols > MAK_MAX_COLS ||
-            (size_t)mak_gemv_nc(q.ncols) * q.geo.k * 2 > (size_t)kLdsBudget ||
-            (q.epi == EPI_SWIGLU && (q.geo.r % 2)))
+            mak_gemv_lds(q) > (size_t)(q.ncols >= 2 ? kLdsBudgetN : kLdsBudget) || q.n_blocks < 1 ||
+            (q.epi == EPI_SWIGLU && (q.geo.r % 2)) ||
+            (q.ncols >= 2 && q.in_kind != IN_RAW && (q.geo.k >> 3) > MAK_NBLOCK))
             return fail(MAK_EINVAL, "internal: bad GEMV phase");
         int rc = launch(m, kind, [&](hipEvent_t e0, hipEvent_t e1) { return mak_launch_gemv(q, m->cur, e0, e1); });
         if (rc) return rc;
@@ -602,7 +606,7 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
         return fail(MAK_ENOMEM, "arena has %zu bytes, needs %zu", arena_bytes, L.total);
 
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    HIP_TRY(mak_set_lds_limit(kLdsBudget, kAttnLdsBudget));
+    HIP_TRY(mak_set_lds_limit(kLdsBudget, kLdsBudgetN, kAttnLdsBudget));
     char* A = reinterpret_cast<char*>(d_arena);
     const int H = c.hidden, d = c.head_dim, I = c.intermediate;
     const int q_dim = c.n_q_heads * d, kv_dim = c.n_kv_heads * d;

@@ -6,6 +6,8 @@
 
 #define MAK_WAVE 64
 #define MAK_BLOCK 256               // threads per workgroup (4 waves)
+#define MAK_GBLOCK 512              // threads per workgroup of the batch-1 GEMV (8 waves, one workgroup per CU)
+#define MAK_NBLOCK 512              // threads per workgroup of the multi-column GEMV (8 waves)
 #define MAK_MAX_COLS 8              // columns (batch rows / prefill tokens) per step
 
 // ---------------------------------------------------------------------------
@@ -86,6 +88,9 @@ struct GemvPhase {
     float* logits;            // EPI_LOGITS destination [col][logits_ld]
     int32_t logits_ld;
     int32_t n_blocks;         // grid size (EPI_LOGITS ticket count)
+    int32_t rr;               // multi-column kernel: rows per lane (a multiple of geo.r)
+    int32_t jw;               // multi-column kernel: waves sharing one tile group (split of K)
+    int32_t threads;          // workgroup size of the launch
     float* part_val;          // EPI_LOGITS per-block partial maxima [n_blocks][MAK_MAX_COLS]
     int32_t* part_idx;
     int32_t* out_tokens;      // EPI_LOGITS: emitted tokens [step][lm_count] (device)
