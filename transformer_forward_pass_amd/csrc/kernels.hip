@@ -74,7 +74,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
     const int rows_it = 4 * rows_w;
     const int sub = lane >> lp_log2, ch = lane & (LP - 1);
     const int my_row = wave * rows_w + sub;
-    constexpr int U = 4;
+    constexpr int U = 8;   // rows per lane per pass: 256 positions per round trip at d = 64
 
     // ---- round trip 1: this column's state
     const ColState cs = p.ctl->cols[col];
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
         const int j = u * rows_it + my_row;
         kpre[u] = make_uint4(0, 0, 0, 0);
         vpre[u] = make_uint4(0, 0, 0, 0);
-        if (j < fp) {
+        if (u * rows_it < fp && j < fp) {   // (the first test is block-uniform: whole passes skip)
             kpre[u] = *reinterpret_cast<const uint4*>(kc_h + (size_t)j * d + ch * 8);
             vpre[u] = *reinterpret_cast<const uint4*>(vc_h + (size_t)j * d + ch * 8);
         }
@@ -168,45 +168,62 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int j = j0 + u * rows_it + my_row;
+            if (j0 + u * rows_it >= n) continue;   // block-uniform: a pass past the last position
             if (j0 == 0) kv[u] = kpre[u];
             else kv[u] = (j < fp) ? *reinterpret_cast<const uint4*>(kc_h + (size_t)j * d + ch * 8)
                                   : make_uint4(0, 0, 0, 0);
             if (j >= fp && j < n) kv[u] = *reinterpret_cast<const uint4*>(kin + (j - fp) * d + ch * 8);
         }
-        double part[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            if (j0 + u * rows_it >= n) continue;
             const uint32_t ku[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
             double a = 0.0;
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 a = fma(qreg[e], (double)((e & 1) ? bf_hi(ku[e >> 1]) : bf_lo(ku[e >> 1])), a);
-            part[u] = a;
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            part[u] = (D_ > 0) ? group_sum<(D_ > 0 ? __builtin_ctz(D_ >> 3) : 0)>(part[u])
-                               : group_sum_rt(part[u], lp_log2);
+            a = (D_ > 0) ? group_sum<(D_ > 0 ? __builtin_ctz(D_ >> 3) : 0)>(a) : group_sum_rt(a, lp_log2);
             const int j = j0 + u * rows_it + my_row;
-            if (ch == 0 && j < n) S[j] = rbf(rbf((float)part[u]) * p.scale);
+            if (ch == 0 && j < n) S[j] = rbf(rbf((float)a) * p.scale);
         }
     }
     __syncthreads();
 
-    // softmax in wave 0: max, e_j = fp32(exp(sigma_j - max)), Z = fp32(sum e_j),
-    // P_j = bf16(fp32(e_j / Z)); each lane rewrites only the entries it reads
-    if (wave == 0) {
+    // softmax over the block: max, e_j = fp32(exp(sigma_j - max)),
+    // Z = fp32(sum e_j), P_j = bf16(fp32(e_j / Z)); each thread rewrites only
+    // the entries it reads
+    if (n <= 256) {   // a short row: one wave, no extra barriers
+        if (wave == 0) {
+            float m = -INFINITY;
+            for (int j = lane; j < n; j += 64) m = fmaxf(m, S[j]);
+            m = wave_max(m);
+            double z = 0.0;
+            for (int j = lane; j < n; j += 64) {
+                const float e = (float)exp((double)S[j] - (double)m);
+                S[j] = e;
+                z += (double)e;
+            }
+            const double Z = (double)(float)wave_sum(z);
+            for (int j = lane; j < n; j += 64) S[j] = rbf((float)((double)S[j] / Z));
+        }
+    } else {
+        __shared__ float redf[MAK_BLOCK / 64];
+        __shared__ double redd[MAK_BLOCK / 64];
         float m = -INFINITY;
-        for (int j = lane; j < n; j += 64) m = fmaxf(m, S[j]);
+        for (int j = tid; j < n; j += MAK_BLOCK) m = fmaxf(m, S[j]);
         m = wave_max(m);
+        if (lane == 0) redf[wave] = m;
+        __syncthreads();
+        m = redf[0];
+        for (int w = 1; w < MAK_BLOCK / 64; w++) m = fmaxf(m, redf[w]);
         double z = 0.0;
-        for (int j = lane; j < n; j += 64) {
+        for (int j = tid; j < n; j += MAK_BLOCK) {
             const float e = (float)exp((double)S[j] - (double)m);
             S[j] = e;
             z += (double)e;
         }
-        const double Z = (double)(float)wave_sum(z);
-        for (int j = lane; j < n; j += 64) S[j] = rbf((float)((double)S[j] / Z));
+        const double Z = (double)(float)block_sum_rt(z, redd, MAK_BLOCK / 64);
+        for (int j = tid; j < n; j += MAK_BLOCK) S[j] = rbf((float)((double)S[j] / Z));
     }
     __syncthreads();
 
@@ -220,6 +237,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int j = j0 + u * rows_it + my_row;
+            if (j0 + u * rows_it >= n) continue;   // block-uniform
             if (j0 == 0) vv[u] = vpre[u];
             else vv[u] = (j < fp) ? *reinterpret_cast<const uint4*>(vc_h + (size_t)j * d + ch * 8)
                                   : make_uint4(0, 0, 0, 0);
@@ -227,6 +245,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
         }
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            if (j0 + u * rows_it >= n) continue;
             const int j = j0 + u * rows_it + my_row;
             const double pj = (j < n) ? (double)S[j] : 0.0;
             const uint32_t vu[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
@@ -462,7 +481,7 @@ hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hi
 }
 
 // dynamic LDS of k_attn: pv[16][d] f64 | qf[d] f32 | kin, vin [8][d] bf16 |
-// rope [9][d/2] bf16 x 2 | S[max_seq] f32
+// rope [9][d/2] bf16 x 2 | S[s_cap] f32
 size_t mak_attn_lds_for(int rep, int d, int max_seq)
 {
     (void)rep;
@@ -472,7 +491,7 @@ size_t mak_attn_lds_for(int rep, int d, int max_seq)
 
 size_t mak_attn_lds(const AttnPhase& p)
 {
-    return mak_attn_lds_for(p.n_q_heads / p.n_kv_heads, p.head_dim, p.max_seq);
+    return mak_attn_lds_for(p.n_q_heads / p.n_kv_heads, p.head_dim, p.s_cap);
 }
 
 #define MAK_ATTN_DIMS(X) X(32) X(64) X(128)

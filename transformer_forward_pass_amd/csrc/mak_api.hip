@@ -24,6 +24,7 @@
 // kernels.hip
 hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+hipError_t mak_launch_attn_split(const AttnPhase& p, int stage, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st, hipEvent_t e0,
                               hipEvent_t e1);
 hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes);
@@ -61,6 +62,11 @@ constexpr int kLdsBudget = 60 * 1024;      // batch-1 GEMV dynamic LDS per workg
 constexpr int kLdsBudgetN = 144 * 1024;    // multi-column GEMV: staged inputs (<= 128 KiB) + partial sums
 constexpr int kLdsInputsN = 128 * 1024;    // multi-column GEMV: NC input rows of K bf16
 constexpr int kAttnLdsBudget = 150 * 1024; // attention dynamic LDS (gfx950: 160 KiB per workgroup)
+constexpr int kAttnSinglePassMax = 4096;   // most positions of the single-pass attention (LDS score row)
+// default split-KV threshold (pos + 1 above it): 48K / head_dim positions,
+// about where the three split launches overtake the single pass (measured:
+// ~300 positions at head_dim 128, ~750 at 64)
+constexpr int kAttnSplitWork = 48 * 1024;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -152,6 +158,8 @@ struct LayerDev {
 struct Layout {
     PackGeom g_embed, g_lm, g_qkv, g_o, g_gu, g_down;
     size_t ctl, out_tokens, x, qkv, o, m, logits, part_val, part_idx;
+    size_t att_sc, att_cmax, att_opart;   // split-KV attention scratch
+    int n_chunks, s_cap;
     size_t cos_t, sin_t, embed, lm_head, final_norm;
     std::vector<LayerDev> layers;
     size_t total;
@@ -178,7 +186,8 @@ int validate_cfg(const mak_config* c)
     if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0f))
         return fail(MAK_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
     if (c->max_seq > (1 << 20)) return fail(MAK_EINVAL, "max_seq too large");
-    const size_t attn_lds = mak_attn_lds_for(c->n_q_heads / c->n_kv_heads, c->head_dim, c->max_seq);
+    const size_t attn_lds = mak_attn_lds_for(c->n_q_heads / c->n_kv_heads, c->head_dim,
+                                             std::min(c->max_seq, kAttnSinglePassMax));
     if (attn_lds > (size_t)kAttnLdsBudget)
         return fail(MAK_EINVAL, "attention workspace (%zu B of LDS) exceeds %d B: lower max_seq",
                     attn_lds, kAttnLdsBudget);
@@ -212,6 +221,11 @@ Layout make_layout(const mak_config* c)
     L.logits = take((size_t)MAK_MAX_COLS * V * 4);
     L.part_val = take((size_t)kMaxGemvBlocks * MAK_MAX_COLS * 4);
     L.part_idx = take((size_t)kMaxGemvBlocks * MAK_MAX_COLS * 4);
+    L.n_chunks = (c->max_seq + MAK_ATTN_CHUNK - 1) / MAK_ATTN_CHUNK;
+    L.s_cap = std::min(c->max_seq, kAttnSinglePassMax);
+    L.att_sc = take((size_t)MAK_MAX_COLS * c->n_q_heads * c->max_seq * 4);
+    L.att_cmax = take((size_t)MAK_MAX_COLS * c->n_q_heads * L.n_chunks * 4);
+    L.att_opart = take((size_t)MAK_MAX_COLS * c->n_q_heads * L.n_chunks * d * 8);
     L.cos_t = take((size_t)c->max_seq * (d / 2) * 2);
     L.sin_t = take((size_t)c->max_seq * (d / 2) * 2);
     L.embed = take((size_t)L.g_embed.bytes);
@@ -259,9 +273,9 @@ struct PhaseTiming {
     int64_t launches[MAK_PHASE_COUNT] = {};
 };
 
-// A captured step: (ncols, lm_begin, lm_count) -> executable graph.
+// A captured step: (ncols, lm_begin, lm_count, split attention) -> executable graph.
 struct StepGraph {
-    int ncols, lm_begin, lm_count;
+    int ncols, lm_begin, lm_count, split;
     hipGraphExec_t exec;
 };
 
@@ -271,6 +285,7 @@ struct mak_model {
     hipStream_t cur = nullptr;       // stream the phase launches go to (capture or model stream)
     hipStream_t capture = nullptr;   // private stream used only to capture step graphs
     bool use_graphs = true;
+    int split_above = 0;                 // split-KV attention once pos + 1 exceeds this
     std::vector<StepGraph> graphs;
     Layout L;
     char* arena;
@@ -364,7 +379,7 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
 // Launch one step of the program on m->cur for the columns currently in the
 // control block: ncols columns; LM head (with argmax feedback) for
 // [lm_begin, lm_begin + lm_count).
-int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens)
+int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, bool split)
 {
     const mak_config& c = m->cfg;
     const Layout& L = m->L;
@@ -416,11 +431,23 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
         a.max_seq = c.max_seq;
         a.eps = c.rms_eps;
         a.scale = (float)(1.0 / std::sqrt((double)d));
+        a.sc = m->at<float>(L.att_sc);
+        a.cmax = m->at<float>(L.att_cmax);
+        a.opart = m->at<double>(L.att_opart);
+        a.n_chunks = L.n_chunks;
+        a.s_cap = L.s_cap;
         if (mak_attn_lds(a) > (size_t)kAttnLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
-        if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
-                 return mak_launch_attn(a, m->cur, e0, e1);
-             })))
+        if (split) {
+            for (int stage = 0; stage < 3; stage++)
+                if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
+                         return mak_launch_attn_split(a, stage, m->cur, e0, e1);
+                     })))
+                    return rc;
+        } else if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
+                        return mak_launch_attn(a, m->cur, e0, e1);
+                    }))) {
             return rc;
+        }
 
         // O + residual
         GemvPhase po{};
@@ -493,21 +520,24 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
 // model's stream, or launch the phases one by one when graphs are off or
 // phase timing is on.  The step reads its per-call state (tokens, positions,
 // slots) from the control block, so one graph serves every step of a shape.
-int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens)
+// max_n = the largest pos + 1 among the step's columns: above the model's
+// threshold (or past the single-pass capacity) attention runs split-KV.
+int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, int max_n)
 {
+    const bool split = max_n > m->split_above || max_n > m->L.s_cap;
     if (!m->use_graphs || m->tm.on) {
         m->cur = m->stream;
-        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens);
+        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split);
     }
     for (const StepGraph& g : m->graphs)
-        if (g.ncols == ncols && g.lm_begin == lm_begin && g.lm_count == lm_count) {
+        if (g.ncols == ncols && g.lm_begin == lm_begin && g.lm_count == lm_count && g.split == (int)split) {
             HIP_TRY(hipGraphLaunch(g.exec, m->stream));
             return MAK_OK;
         }
     hipGraph_t graph = nullptr;
     HIP_TRY(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal));
     m->cur = m->capture;
-    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens);
+    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split);
     hipError_t e = hipStreamEndCapture(m->capture, &graph);
     m->cur = m->stream;
     if (rc) {
@@ -515,7 +545,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         return rc;
     }
     if (e != hipSuccess) return fail(MAK_EDEVICE, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
-    StepGraph sg{ncols, lm_begin, lm_count, nullptr};
+    StepGraph sg{ncols, lm_begin, lm_count, (int)split, nullptr};
     e = hipGraphInstantiate(&sg.exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return fail(MAK_EDEVICE, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
@@ -551,7 +581,7 @@ int prefill_chunks(mak_model* m, int slot, const int32_t* ids, int n, int start_
         int rc = set_cols(m, cols, T, step0);
         if (rc) return rc;
         const bool last = c0 + T >= n;
-        rc = run_step(m, T, T - 1, (last && want_lm) ? 1 : 0, m->at<int32_t>(m->L.out_tokens));
+        rc = run_step(m, T, T - 1, (last && want_lm) ? 1 : 0, m->at<int32_t>(m->L.out_tokens), start_pos + c0 + T);
         if (rc) return rc;
     }
     return MAK_OK;
@@ -670,6 +700,7 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
     m->arena_bytes = arena_bytes;
     m->stream = st;
     m->slot_len.assign(c.max_batch, 0);
+    m->split_above = kAttnSplitWork / c.head_dim;
     m->cur = st;
     if (hipStreamCreateWithFlags(&m->capture, hipStreamNonBlocking) != hipSuccess) {
         delete m;
@@ -721,6 +752,15 @@ int mak_set_executor(mak_model* m, int executor)
     if (executor != MAK_EXEC_GRAPH && executor != MAK_EXEC_PHASED)
         return fail(MAK_EINVAL, "unknown executor %d", executor);
     m->use_graphs = executor == MAK_EXEC_GRAPH;
+    return MAK_OK;
+}
+
+int mak_set_attention_split(mak_model* m, int32_t above)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    if (above < 0) return fail(MAK_EINVAL, "split threshold %d < 0", above);
+    m->split_above = above;
     return MAK_OK;
 }
 
@@ -803,7 +843,7 @@ int mak_decode_step(mak_model* m, int32_t slot, int32_t token, int32_t pos, floa
     cs.first_pos = pos;
     cs.first_col = 0;
     if ((rc = set_cols(m, &cs, 1, 0))) return rc;
-    if ((rc = run_step(m, 1, 0, 1, m->at<int32_t>(m->L.out_tokens)))) return rc;
+    if ((rc = run_step(m, 1, 0, 1, m->at<int32_t>(m->L.out_tokens), pos + 1))) return rc;
     if (d_logits)
         HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)c.vocab * 4,
                                hipMemcpyDeviceToDevice, m->stream));
@@ -832,8 +872,8 @@ int mak_generate(mak_model* m, int32_t slot, const int32_t* prompt, int32_t n, i
     m->slot_len[slot] = 0;
     if ((rc = prefill_chunks(m, slot, prompt, n, 0, true, 0))) return rc;
     int32_t* d_out = m->at<int32_t>(m->L.out_tokens);
-    for (int s = 1; s < max_new; s++)
-        if ((rc = run_step(m, 1, 0, 1, d_out))) return rc;
+    for (int s = 1; s < max_new; s++)   // the token at position n + s - 1
+        if ((rc = run_step(m, 1, 0, 1, d_out, n + s))) return rc;
     HIP_TRY(hipMemcpyAsync(out_tokens, d_out, (size_t)max_new * 4, hipMemcpyDeviceToHost, m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
     if ((rc = collect_timing(m))) return rc;
@@ -870,8 +910,10 @@ int mak_decode_batch(mak_model* m, int32_t B, const int32_t* slots, const int32_
     }
     if ((rc = set_cols(m, cols, B, 0))) return rc;
     int32_t* d_out = m->at<int32_t>(m->L.out_tokens);
+    int max_pos = 0;
+    for (int b = 0; b < B; b++) max_pos = std::max(max_pos, (int)positions[b]);
     for (int s = 0; s < steps; s++)
-        if ((rc = run_step(m, B, 0, B, d_out))) return rc;
+        if ((rc = run_step(m, B, 0, B, d_out, max_pos + s + 1))) return rc;
     HIP_TRY(hipMemcpyAsync(out_tokens, d_out, (size_t)steps * B * 4, hipMemcpyDeviceToHost, m->stream));
     if (d_logits)
         HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)B * c.vocab * 4,

@@ -9,6 +9,7 @@
 #define MAK_GBLOCK 512              // threads per workgroup of the batch-1 GEMV (8 waves, one workgroup per CU)
 #define MAK_NBLOCK 512              // threads per workgroup of the multi-column GEMV (8 waves)
 #define MAK_MAX_COLS 8              // columns (batch rows / prefill tokens) per step
+#define MAK_ATTN_CHUNK 128          // positions per chunk of the split-KV attention
 
 // ---------------------------------------------------------------------------
 // Packed weight geometry.
@@ -112,4 +113,10 @@ struct AttnPhase {
     int32_t n_q_heads, n_kv_heads, head_dim, max_seq;
     float eps;
     float scale;              // fp32(1/sqrt(head_dim))
+    // split-KV attention (long contexts) scratch
+    float* sc;                // scores [col][Hq][max_seq]
+    float* cmax;              // chunk maxima [col][Hq][n_chunks]
+    double* opart;            // partial outputs [col][Hq][n_chunks][head_dim]
+    int32_t n_chunks;         // ceil(max_seq / MAK_ATTN_CHUNK)
+    int32_t s_cap;            // single-pass kernel: most positions its LDS score row holds
 };
