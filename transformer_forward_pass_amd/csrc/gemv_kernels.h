@@ -104,7 +104,8 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
             for (int q = tid + QPT * NT; q < C; q += NT) h4[q] = src[q];
             continue;
         }
-        // RMSNorm of x (K <= 4096: at most 2 chunks per thread)
+        // RMSNorm of x: at most 2 chunks per thread (launches size the
+        // workgroup so that 16 * NT >= K)
         double ss = 0.0;
 #pragma unroll
         for (int i = 0; i < 2; i++) {

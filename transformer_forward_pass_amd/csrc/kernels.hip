@@ -455,8 +455,19 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
         return (int)std::max<int64_t>(1, std::min<int64_t>((tiles + wpb - 1) / wpb, std::min(per_cu * n_cu, cap)));
     }
     if (tiles <= 8 * (int64_t)n_cu) {
-        p.threads = 256;
-        return (int)std::min<int64_t>((tiles + 3) / 4, cap);
+        // waves per workgroup: small matrices spread over more CUs in
+        // workgroups of 2 waves (measured faster up to ~1024 tiles), larger
+        // ones in workgroups of 4 (MAK_GEMV_STATIC_WAVES overrides: 1, 2, 4)
+        static int sw = -1;
+        if (sw < 0) {
+            const char* e = getenv("MAK_GEMV_STATIC_WAVES");
+            sw = (e && (atoi(e) == 1 || atoi(e) == 2 || atoi(e) == 4)) ? atoi(e) : 0;
+        }
+        // RMSNorm staging holds 2 chunks of 8 inputs per thread
+        int w = sw ? sw : (tiles <= 1024 ? 2 : 4);
+        while (p.in_kind != IN_RAW && w < 4 && 64 * w * 16 < p.geo.k) w *= 2;
+        p.threads = 64 * w;
+        return (int)std::min<int64_t>((tiles + w - 1) / w, cap);
     }
     const int j = (p.geo.k >> 3) >> p.geo.lr_log2;
     p.threads = gemv1_waves(p.geo.r, j) * 64;
