@@ -10,9 +10,10 @@ after a 32-token prompt, section "Measured").
 
 Also printed, in the same JSON line:
   roofline      -- the dominant kernel (the phase kind with the largest total
-                   time) measured with HIP events on the model's stream over
-                   a second pass of the same K steps: algorithmic bytes per
-                   launch / average launch duration, against 8 TB/s.
+                   GPU time: a GEMV kind or attention) measured with HIP events
+                   on the model's stream over a second pass of the same K
+                   steps: algorithmic bytes per launch / average launch
+                   duration, against 8 TB/s.
   cpu_baseline  -- the CPU oracle on a bounded sample of the same workload.
   token_roofline -- bytes one decode token must stream (weights + KV) per
                    steady-state decode token time, against 8 TB/s.
@@ -79,6 +80,28 @@ def _gemv_bytes(shape, kind):
     return None
 
 
+def _attn_bytes(shape, p0, n_new, chunk=8):
+    """Algorithmic bytes of the attention launches of one generate call
+    (prompt of p0 tokens in chunks, then n_new - 1 decode steps), and their
+    number of launches: per step, the K and V rows of every kv head at the
+    positions attended (each read once), the step's q/k/v rows, the K/V
+    appends and the attention output (bf16)."""
+    d, Hq, Hkv = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    row = d * 2
+    total, steps = 0, 0
+    def step(n_ctx, cols):
+        return (2 * Hkv * n_ctx * row + cols * (Hq + 2 * Hkv) * row + cols * 2 * Hkv * row
+                + cols * Hq * row)
+    for t0 in range(0, p0, chunk):
+        T = min(chunk, p0 - t0)
+        total += step(t0 + T, T)
+        steps += 1
+    for i in range(n_new - 1):
+        total += step(p0 + i + 1, 1)
+        steps += 1
+    return total * shape.n_layers, steps * shape.n_layers
+
+
 def run_gpu(args, shape, wl, w, prompt, steps):
     import torch
     from transformer_forward_pass_amd import mak
@@ -125,10 +148,14 @@ def measure(args, name, steps):
     dt, t_prefill, times = run_gpu(args, shape, wl, w, prompt, steps)
     p0, n = len(prompt), wl.max_new
     t_decode = (dt / steps - t_prefill) / (n - 1)
-    kinds = [k for k in ("qkv", "o", "gateup", "down", "lmhead") if times[k][1]]
+    kinds = [k for k in ("qkv", "attn", "o", "gateup", "down", "lmhead") if times[k][1]]
     dom = max(kinds, key=lambda k: times[k][0])
     avg_s = times[dom][0] / times[dom][1] / 1e3
-    per_launch = _gemv_bytes(shape, dom)
+    if dom == "attn":
+        tot, launches = _attn_bytes(shape, p0, n)
+        per_launch = tot // launches
+    else:
+        per_launch = _gemv_bytes(shape, dom)
     achieved = per_launch / avg_s / 1e9
     avg_pos = p0 + (n - 2) / 2.0
     tok_bytes = shape.streamed_weight_bytes() + shape.kv_bytes_per_position() * (avg_pos + 1)
