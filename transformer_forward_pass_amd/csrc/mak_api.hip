@@ -99,13 +99,11 @@ PackGeom make_geom(int64_t n, int k, bool pairs)
     const int lr = gcd(C, 64);
     g.lr_log2 = ilog2(lr);
     const int G = 64 / lr;
+    // two rows per lane group once that still leaves >= 2048 tiles: more,
+    // smaller tiles keep each wave's batches flowing (measured faster than
+    // four rows on the 1B-class shapes, e.g. gate/up 20.4 -> 18.2 us)
     int r = pairs ? 2 : 1;
-    for (int cand : {4, 2}) {
-        if ((n + (int64_t)G * cand - 1) / ((int64_t)G * cand) >= 2048) {
-            r = cand;
-            break;
-        }
-    }
+    if ((n + (int64_t)G * 2 - 1) / ((int64_t)G * 2) >= 2048) r = 2;
     g.r = r;
     const int64_t rows_per_tile = (int64_t)G * r;
     g.n_tiles = (int32_t)((n + rows_per_tile - 1) / rows_per_tile);
