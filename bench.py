@@ -186,6 +186,105 @@ def cpu_baseline(shape, w, prompt, n_new):
                 len(prompt), n_new, dt)}
 
 
+def measure_batched(args, name="tinyllama-1.1b", reps=2):
+    """Batched decode (8 sequences with their own slots and positions, one
+    multi-column step per token): aggregate tok/s over 127 steps after each
+    sequence's prompt is prefilled, plus per-phase times and the dominant
+    GEMV's roofline over a timed pass of 16 steps."""
+    import torch
+    from transformer_forward_pass_amd import mak, synth
+    wl = synth.WORKLOADS[name]
+    shape = wl.shape
+    w = synth.make_weights(shape)
+    prompts = synth.make_prompts(wl)
+    B = len(prompts)
+    m = mak.MakModel(shape, w, device="cuda:0", max_seq=shape.max_seq, max_batch=B)
+    first = [int(torch.argmax(m.prefill(p, slot=b)).item()) for b, p in enumerate(prompts)]
+    pos = [len(p) for p in prompts]
+    steps = wl.max_new - 1
+    m.decode_batch(first, pos, steps=2, want_logits=False)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        ev0.record()
+        m.decode_batch(first, pos, steps=steps, want_logits=False)
+        ev1.record()
+        torch.cuda.synchronize()
+        t = ev0.elapsed_time(ev1) / 1e3
+        best = t if best is None else min(best, t)
+    m.set_phase_timing(True)
+    m.decode_batch(first, pos, steps=16, want_logits=False)
+    times = m.phase_times()
+    m.set_phase_timing(False)
+    m.free()
+    kinds = [k for k in ("qkv", "o", "gateup", "down", "lmhead") if times[k][1]]
+    dom = max(kinds, key=lambda k: times[k][0])
+    avg_s = times[dom][0] / times[dom][1] / 1e3
+    per_launch = _gemv_bytes(shape, dom)
+    avg_ctx = sum(pos) / B + steps / 2.0
+    step_bytes = shape.streamed_weight_bytes() + shape.kv_bytes_per_position() * avg_ctx * B
+    t_step = best / steps
+    return {"workload": "%s-shaped random-init decoder: %d sequences (prompts of %d..%d tokens), "
+                        "%d greedy tokens each decoded together" % (name, B, min(pos), max(pos), wl.max_new),
+            "value": round(B * steps / best, 2), "unit": "tok/s (all sequences)",
+            "ms_per_step": round(t_step * 1e3, 4),
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(per_launch / avg_s / 1e9, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(per_launch / avg_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 3),
+                         "launches": times[dom][1]},
+            "step_roofline": {"bytes_per_step": int(step_bytes),
+                              "achieved_gbs": round(step_bytes / t_step / 1e9, 2),
+                              "frac": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4)},
+            "phase_ms_per_step": {k: round(v[0] / 16, 4) for k, v in times.items()}}
+
+
+def measure_long(args, name="qwen3-0.6b", reps=2):
+    """Long context: a 512-token prompt in 64 chunks of 8, then 256 greedy
+    tokens (attention runs split-KV past 384 positions at head_dim 128)."""
+    import torch
+    from transformer_forward_pass_amd import mak, synth
+    wl = synth.WORKLOADS[name]
+    shape = wl.shape
+    w = synth.make_weights(shape)
+    prompt = synth.make_prompts(wl)[0]
+    m = mak.MakModel(shape, w, device="cuda:0", max_seq=shape.max_seq)
+    m.generate(prompt, 8)
+    torch.cuda.synchronize()
+    best = bestp = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        m.generate(prompt, wl.max_new)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t0
+        best = t if best is None else min(best, t)
+        t0 = time.perf_counter()
+        m.prefill(prompt, want_logits=False)
+        torch.cuda.synchronize()
+        tp = time.perf_counter() - t0
+        bestp = tp if bestp is None else min(bestp, tp)
+    m.set_phase_timing(True)
+    m.generate(prompt, wl.max_new)
+    times = m.phase_times()
+    m.set_phase_timing(False)
+    m.free()
+    t_dec = (best - bestp) / (wl.max_new - 1)
+    p0, n = len(prompt), wl.max_new
+    avg_ctx = p0 + n / 2.0
+    tok_bytes = shape.streamed_weight_bytes() + shape.kv_bytes_per_position() * avg_ctx
+    prefill_bytes = (p0 // 8) * shape.streamed_weight_bytes() * 1.0
+    return {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of 8) + %d greedy tokens, "
+                        "batch 1" % (name, p0, n),
+            "value": round(n / best, 2), "unit": "tok/s",
+            "decode_tok_s": round(1.0 / t_dec, 2), "prefill_ms": round(bestp * 1e3, 3),
+            "token_roofline": {"bytes_per_token": int(tok_bytes),
+                               "achieved_gbs": round(tok_bytes / t_dec / 1e9, 2),
+                               "frac": round(tok_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4)},
+            "prefill_weight_gbs": round(prefill_bytes / bestp / 1e9, 2),
+            "phase_ms_per_call": {k: round(v[0], 4) for k, v in times.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +293,8 @@ def main():
     ap.add_argument("--cpu-new", type=int, default=24, help="greedy tokens of the CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 1B-shape measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the batched-decode and long-context measurements")
     ap.add_argument("--max-new", type=int, default=0,
                     help="override the greedy token count (short counter-collection runs only)")
     args = ap.parse_args()
@@ -238,6 +339,9 @@ def main():
                             "ms_per_step": round(r2["ms_per_step"], 4),
                             "roofline": r2["roofline"], "token_roofline": r2["token_roofline"],
                             "phase_ms_per_step": r2["phase_ms_per_step"]}
+    if not args.no_extra and not args.max_new:
+        out["batched"] = measure_batched(args)
+        out["long_context"] = measure_long(args)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(r["shape"], r["w"], r["prompt"], args.cpu_new)
     print(json.dumps(out))

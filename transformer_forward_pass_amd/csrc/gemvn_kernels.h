@@ -12,7 +12,8 @@
 //    each converted weight serves NC columns;
 //  * a group of RR/R tiles can be shared by JW waves of the workgroup, each
 //    taking every JW-th chunk iteration (a split of K); their row sums are
-//    combined through LDS in wave order after the lane-group reduction;
+//    combined through LDS in wave order after a reduce-scatter over the
+//    lanes of each row, which also spreads the epilogue over those lanes;
 //  * the NC input rows (RMSNorm applied) are staged once per workgroup in
 //    LDS with a single barrier for all columns' statistics.
 #pragma once
@@ -138,12 +139,78 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Dynamic LDS of k_gemvn: staged inputs, then every wave's row sums [wave][group][RR*NC].
-__host__ __device__ inline size_t gemvn_part_offset(int nc, int k) { return ((size_t)nc * k * 2 + 15) & ~(size_t)15; }
-__host__ __device__ inline size_t gemvn_lds(int nc, int k, int rr, int lr_log2)
+// Values a lane keeps after the reduce-scatter of V = rr*nc row sums over
+// 2^lr_log2 lanes (SwiGLU keeps gate/up pairs together: one halving fewer).
+__host__ __device__ inline int gemvn_kept(int rr, int nc, int lr_log2, bool pairs)
 {
-    const size_t g = (size_t)64 >> lr_log2;
-    return gemvn_part_offset(nc, k) + (size_t)(MAK_NBLOCK / 64) * g * rr * nc * sizeof(double);
+    int logv = 0;
+    while ((1 << logv) < rr * nc) logv++;
+    const int h = lr_log2 < logv - (pairs ? 1 : 0) ? lr_log2 : logv - (pairs ? 1 : 0);
+    return (rr * nc) >> h;
+}
+
+// Dynamic LDS of k_gemvn: staged inputs, then (waves sharing a group only)
+// every wave's kept sums [wave][kept][lane].
+__host__ __device__ inline size_t gemvn_part_offset(int nc, int k) { return ((size_t)nc * k * 2 + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t gemvn_lds(int nc, int k, int rr, int jw, int lr_log2, bool pairs)
+{
+    return gemvn_part_offset(nc, k) +
+           (jw > 1 ? (size_t)(MAK_NBLOCK / 64) * gemvn_kept(rr, nc, lr_log2, pairs) * 64 * sizeof(double) : 0);
+}
+
+// xor-lane exchange of a double at distance 2^K (inside 64 lanes)
+template <int K>
+__device__ __forceinline__ double xor_lanes(double v)
+{
+    if (K == 0) return dpp_d<DPP_XOR1>(v);
+    if (K == 1) return dpp_d<DPP_XOR2>(v);
+    if (K == 3) return dpp_d<DPP_ROR8>(v);   // rotating a 16-lane row by 8 is xor 8
+    if (K == 2) {
+        const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(v), 0x101F);   // xor 4 within 32 lanes
+        const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(v), 0x101F);
+        return __hiloint2double(hi, lo);
+    }
+    return __shfl_xor(v, 1 << K, 64);
+}
+
+// Reduce-scatter of a[0..V) over the 2^lrl lanes of each row group, lane
+// bits from the lowest up: at level k a lane keeps the half of its list
+// selected by its bit k and adds the partner's copy of that half.  After
+// min(lrl, HM) halvings (HM = log2 V, one less to keep pairs) the lane holds
+// the full sums of a[0..V >> that) at list positions
+// i + sum_k bit_k(lane) * (V >> (k + 1)); further levels (lrl > HM) add the
+// remaining values over the rest of the group.  Every sum uses the same tree
+// in every group; sums are exact in fp64, so the tree does not matter.
+template <int V, int HM, int K>
+__device__ __forceinline__ void rs_level(double (&a)[V], int lrl, int lane)
+{
+    if (K >= lrl) return;
+    if (K < HM) {
+        constexpr int n = V >> K, half = n >> 1;
+        const bool up = (lane >> K) & 1;
+#pragma unroll
+        for (int i = 0; i < half; i++) {
+            const double lo = a[i], hi = a[i + half];
+            const double send = up ? lo : hi;
+            const double keep = up ? hi : lo;
+            a[i] = keep + xor_lanes<K>(send);
+        }
+    } else {
+        constexpr int n = V >> HM;
+#pragma unroll
+        for (int i = 0; i < n; i++) a[i] += xor_lanes<K>(a[i]);
+    }
+}
+
+template <int V, int HM>
+__device__ __forceinline__ void reduce_scatter(double (&a)[V], int lrl, int lane)
+{
+    rs_level<V, HM, 0>(a, lrl, lane);
+    rs_level<V, HM, 1>(a, lrl, lane);
+    rs_level<V, HM, 2>(a, lrl, lane);
+    rs_level<V, HM, 3>(a, lrl, lane);
+    rs_level<V, HM, 4>(a, lrl, lane);
+    rs_level<V, HM, 5>(a, lrl, lane);
 }
 
 // Work split.  A group is RR/R consecutive tiles; unit (group, j) is the RR
@@ -155,6 +222,8 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
 {
     constexpr int NW = MAK_NBLOCK / 64;
     constexpr int V = RR * NC;
+    constexpr int LOGV = (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
+    constexpr int HM = (EPI == EPI_SWIGLU) ? LOGV - 1 : LOGV;   // halvings at most
     constexpr int QB = (NC <= 2) ? 16 : (NC <= 4) ? 8 : 4;   // 16-byte loads per lane per batch
     constexpr int UB = (QB / RR) > 0 ? QB / RR : 1;        // units per batch
     static_assert(UB * RR == QB, "batch must hold whole units");
@@ -265,11 +334,11 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
         }
     };
 
-    // 3. a finished group: reduce each row over its lanes; lane s == 0 of
-    //    every row group parks the wave's V sums in LDS; after a barrier the
-    //    first wave of the group slot adds the JW waves' sums in wave order,
-    //    the lanes of a row group splitting the V values (SwiGLU: the V/2
-    //    gate/up pairs), and applies the epilogue to each.
+    // 3. a finished group: a reduce-scatter over each row's lanes leaves
+    //    every lane the full sums of its share of the V values; with JW > 1
+    //    waves on the group, the first wave adds the others' shares (same
+    //    lane, same values) in wave order through LDS; then each lane
+    //    applies the epilogue to its values (SwiGLU: gate/up pairs).
     auto epilogue_value = [&](int g, int u, int c, double y, double y_up) __attribute__((always_inline)) {
         const int64_t t = (int64_t)g * TU + (u >> rl);
         const int64_t row = t * G * R + grp * R + (u & (R - 1));
@@ -290,46 +359,61 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
             const float v = (float)y;
             p.logits[(size_t)c * p.logits_ld + row] = v;
 #pragma unroll
-            for (int cc = 0; cc < NC; cc++) {
-                if (cc == c && (v > best_v[cc] || (v == best_v[cc] && (int)row < best_i[cc]))) {
-                    best_v[cc] = v;
-                    best_i[cc] = (int)row;
-                }
+            for (int cc = 0; cc < NC; cc++) {   // (selects, not an indexed update)
+                const bool take = cc == c && (v > best_v[cc] || (v == best_v[cc] && (int)row < best_i[cc]));
+                best_v[cc] = take ? v : best_v[cc];
+                best_i[cc] = take ? (int)row : best_i[cc];
             }
         }
     };
     auto finish_group = [&](int round) __attribute__((always_inline)) {
         const int g = group_at(round);
-        group_sum_all<V>(reinterpret_cast<double(&)[V]>(acc), lrl);
-        if (s == 0) {
-            double* mine = part + ((size_t)wave * G + grp) * V;
+        // list order c*RR + u keeps each gate/up pair (u, u+1) adjacent
+        double a[V];
 #pragma unroll
-            for (int u = 0; u < RR; u++)
+        for (int u = 0; u < RR; u++)
 #pragma unroll
-                for (int c = 0; c < NC; c++) mine[u * NC + c] = acc[u][c];
-        }
-        // JW == 1: the wave reads back only what it wrote itself
-        if (JW > 1) __syncthreads();
-        else wave_sync_lds();
-        if (wj == 0 && g < NG) {
-            const double* base = part + ((size_t)wave * G + grp) * V;
-            const size_t wstride = (size_t)G * V;
-            constexpr int NVAL = (EPI == EPI_SWIGLU) ? V / 2 : V;
-            for (int k = s; k < NVAL; k += lr) {
-                // SwiGLU: pair k -> rows u = 2*(k / NC), u + 1 of column k % NC
-                const int c = k % NC;
-                const int u = (EPI == EPI_SWIGLU) ? 2 * (k / NC) : k / NC;
-                const int v = u * NC + c;
-                double y = 0.0, y_up = 0.0;
-                for (int w2 = 0; w2 < JW; w2++) {
-                    y += base[w2 * wstride + v];
-                    if (EPI == EPI_SWIGLU) y_up += base[w2 * wstride + v + NC];
+            for (int c = 0; c < NC; c++) a[c * RR + u] = acc[u][c];
+        reduce_scatter<V, HM>(a, lrl, lane);
+        const int hk = lrl < HM ? lrl : HM;
+        const int nk = V >> hk;                           // values this lane keeps
+        int off = 0;
+        for (int k = 0; k < hk; k++) off += ((s >> k) & 1) * (V >> (k + 1));
+        // only the first lane of each residue class past the halvings applies them
+        const bool lead = (s >> hk) == 0;
+        if (JW > 1) {
+#pragma unroll
+            for (int i = 0; i < V; i++)
+                if (i < nk) part[((size_t)wave * nk + i) * 64 + lane] = a[i];
+            __syncthreads();
+            if (wj == 0) {
+#pragma unroll
+                for (int i = 0; i < V; i++) {
+                    if (i >= nk) continue;
+                    double y = 0.0;
+                    for (int w2 = 0; w2 < JW; w2++) y += part[((size_t)(wave + w2) * nk + i) * 64 + lane];
+                    a[i] = y;
                 }
-                epilogue_value(g, u, c, y, y_up);
+            }
+        }
+        if (wj == 0 && g < NG && lead) {
+            if (EPI == EPI_SWIGLU) {
+#pragma unroll
+                for (int i = 0; i + 1 < V; i += 2) {
+                    if (i >= nk) continue;
+                    const int idx = off + i;                  // even: gate row u, up row u + 1
+                    epilogue_value(g, idx % RR, idx / RR, a[i], a[i + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; i++) {
+                    if (i >= nk) continue;
+                    const int idx = off + i;
+                    epilogue_value(g, idx % RR, idx / RR, a[i], 0.0);
+                }
             }
         }
         if (JW > 1) __syncthreads();   // `part` is rewritten by the next round
-        else wave_sync_lds();
 #pragma unroll
         for (int u = 0; u < RR; u++)
 #pragma unroll

@@ -359,7 +359,8 @@ static int gemv_threads(const GemvPhase& p) { return p.threads; }
 
 size_t mak_gemv_lds(const GemvPhase& p)
 {
-    if (p.ncols >= 2) return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.geo.lr_log2);
+    if (p.ncols >= 2)
+        return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.jw, p.geo.lr_log2, p.epi == EPI_SWIGLU);
     return (size_t)p.geo.k * sizeof(uint16_t);
 }
 
@@ -394,8 +395,8 @@ static int resident_blocks(const void* fn, int threads, size_t lds)
 }
 
 // Multi-column work split: rows per lane rr (as many as keep >= 1024 tile
-// groups and fit the LDS budget), then waves per group jw (a power of two <=
-// the chunk iterations) until about 2048 waves are busy.
+// groups), then waves per group jw (a power of two <= the chunk iterations,
+// within the LDS budget) until about 2048 waves are busy.
 static void gemvn_plan(GemvPhase& p, size_t lds_budget)
 {
     const int nc = mak_gemv_nc(p.ncols);
@@ -405,14 +406,16 @@ static void gemvn_plan(GemvPhase& p, size_t lds_budget)
     int rr = R;
     for (int cand : {4, 2}) {
         if (cand < R || cand % R) continue;
-        if ((tiles + cand / R - 1) / (cand / R) >= 1024 && gemvn_lds(nc, p.geo.k, cand, lrl) <= lds_budget) {
+        if ((tiles + cand / R - 1) / (cand / R) >= 1024) {
             rr = cand;
             break;
         }
     }
     const int64_t ng = (tiles + rr / R - 1) / (rr / R);
     int jw = 1;
-    while (jw * 2 <= MAK_NBLOCK / 64 && jw * 2 <= J && ng * jw < 2048) jw *= 2;
+    while (jw * 2 <= MAK_NBLOCK / 64 && jw * 2 <= J && ng * jw < 2048 &&
+           gemvn_lds(nc, p.geo.k, rr, jw * 2, lrl, p.epi == EPI_SWIGLU) <= lds_budget)
+        jw *= 2;
     p.rr = rr;
     p.jw = jw;
 }
