@@ -31,15 +31,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_smollm2-135m.md")
-TRAFFIC_SOURCES = ["gemv_kernels.h", "device_math.h", "mak_internal.h", "gemv1_swiglu.hip", "gemv1_store.hip",
-                   "gemv1_residual.hip", "gemv1_logits.hip", "kernels.hip"]
+TRAFFIC_SOURCES = ["gemv_kernels.h", "gemvn_kernels.h", "device_math.h", "mak_internal.h", "gemv1_swiglu.hip",
+                   "gemv1_store.hip", "gemv1_residual.hip", "gemv1_logits.hip", "kernels.hip", "attn_split.hip"]
 
 
 def measured_traffic(kind):
-    """HBM bytes per launch of `kind` from the committed rocprofv3 counter
-    summary (FETCH_SIZE / WRITE_SIZE, calibrated against a copy of known
-    size), or None when the summary is for another kernel kind or the kernel
-    sources have changed since the counters were taken."""
+    """HBM bytes per launch of phase kind `kind` from the committed rocprofv3
+    counter summary (FETCH_SIZE/WRITE_SIZE scaled by a copy of known size),
+    or None when the summary is missing or the kernel sources changed since
+    the counters were taken."""
     import hashlib
     try:
         text = open(TRAFFIC_FILE).read()
@@ -48,18 +48,16 @@ def measured_traffic(kind):
     vals = {}
     for line in text.splitlines():
         line = line.strip()
-        for key in ("kernel_kind", "traffic_bytes_per_launch", "source_sha256"):
-            if line.startswith(key + ":"):
-                vals[key] = line.split(":", 1)[1].strip()
+        if ":" in line and not line.startswith("|"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "transformer_forward_pass_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if vals.get("kernel_kind") != kind or vals.get("source_sha256") != h.hexdigest():
+    if vals.get("source_sha256") != h.hexdigest() or ("traffic." + kind) not in vals:
         return None
-    return int(vals["traffic_bytes_per_launch"])
-WORKLOAD = "smollm2-135m"
-SECONDARY = "llama-3.2-1b"
+    return int(float(vals["traffic." + kind]))
 
 
 def _gemv_bytes(shape, kind):

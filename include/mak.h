@@ -26,9 +26,9 @@
  *
  * Arithmetic: bf16 storage, fp64 accumulation of every dot product and fp64
  * evaluation of exp/sqrt, with bf16 rounding at the op boundaries of eager
- * bf16 execution ("model-as-a-kernel", Method section: arithmetic reproduces
- * eager bf16 semantics op for op, fixed reduction trees, no floating-point
- * atomics, bitwise deterministic output).
+ * bf16 execution ("model-as-a-kernel", Method section: every operation rounds
+ * as an eager bf16 run does; reductions use fixed trees and no floating-point
+ * atomics, so the output is bitwise deterministic).
  */
 #ifndef MAK_H
 #define MAK_H

@@ -10,14 +10,14 @@
  *     ["Building a GPU compiler from scratch ... (Emmy)", Tensor IR section].
  *   - Decoder block: RMSNorm blocks, rotary attention with GQA, optional
  *     per-head qk RMSNorm, SwiGLU MLP, plain unscaled rope, LM head and
- *     greedy argmax, arithmetic following transformers' eager bf16 semantics
- *     op for op ["model-as-a-kernel", API and Method sections].
+ *     greedy argmax, each operation rounded to bf16 where an eager bf16
+ *     reference run rounds it ["model-as-a-kernel", API and Method sections].
  *   - Masked positions contribute nothing to the softmax (the causal-mask
  *     argument of "GPT-2 on the GPU", section "The Whole Model as One
  *     Kernel").
  *
- * Rounding schedule (our reading of "eager bf16 semantics"; the pages do not
- * list the rounding points):
+ * Rounding schedule (our reading of the card's eager-bf16 claim; the pages
+ * do not list the rounding points):
  *   r32(v) = round-to-nearest-even to fp32, rbf(v) = bf16(RNE) of r32(v).
  *   A dot product of bf16 vectors is the fp64 sum of the (exact) products in
  *   ascending index order.  Transcendentals are evaluated in fp64 on the

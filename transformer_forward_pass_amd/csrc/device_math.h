@@ -4,8 +4,8 @@
 // Rounding schedule: every dot product is accumulated in fp64 (products of
 // two bf16 values are exact in fp64) and rounded once to fp32, then to bf16
 // where a tensor is stored in bf16; exp/sqrt are evaluated in fp64 on fp32
-// operands.  This reproduces eager bf16 execution op for op ("model-as-a-
-// kernel", Method section) up to fp64 rounding, i.e. the bf16 decisions are
+// operands.  Each operation thus rounds as eager bf16 execution does
+// ("model-as-a-kernel", Method section) up to fp64 rounding: the bf16 decisions are
 // the same as an ascending-order exact evaluation except in vanishingly rare
 // ties.  (fp32 accumulation was measured to flip enough bf16 roundings to
 // move whole-model logits by ~1e-2 relative on the 135M shape.)
