@@ -60,6 +60,10 @@ def measured_traffic(kind):
     return int(float(vals["traffic." + kind]))
 
 
+WORKLOAD = "smollm2-135m"
+SECONDARY = "llama-3.2-1b"
+
+
 def _gemv_bytes(shape, kind):
     """Algorithmic bytes of one launch of a phase kind at batch 1: weight
     bytes streamed once + activation vectors read and written (bf16)."""

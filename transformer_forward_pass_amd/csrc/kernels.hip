@@ -345,7 +345,7 @@ static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn(p) != nullptr; 
 
 static const void* gemv_fn(const GemvPhase& p)
 {
-    if (p.ncols >= 2) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
+    if (p.multi) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
     if (const void* f = gemv1_fn(p)) return f;
     switch (p.geo.r) {
     case 1: return gemv_fn_r1<1>(p.epi);
@@ -359,7 +359,7 @@ static int gemv_threads(const GemvPhase& p) { return p.threads; }
 
 size_t mak_gemv_lds(const GemvPhase& p)
 {
-    if (p.ncols >= 2)
+    if (p.multi)
         return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.jw, p.geo.lr_log2, p.epi == EPI_SWIGLU);
     return (size_t)p.geo.k * sizeof(uint16_t);
 }
@@ -428,7 +428,10 @@ static void gemvn_plan(GemvPhase& p, size_t lds_budget)
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
 {
     const int n_cu = device_cus();
-    if (p.ncols >= 2) {
+    // (splitting one-column tiles over several waves with this kernel was
+    // measured slower: its staging and combine cost more than the fold)
+    p.multi = p.ncols >= 2;
+    if (p.multi) {
         gemvn_plan(p, lds_budget_n);
         p.threads = MAK_NBLOCK;
         const void* fn = gemv_fn(p);

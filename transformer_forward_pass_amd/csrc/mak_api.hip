@@ -364,9 +364,9 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
             return fail(MAK_EINVAL, "internal: LM head split");
         // host-side shape checks of what the kernel assumes
         if (q.geo.k % 8 || q.ncols < 1 || q.ncols > MAK_MAX_COLS || q.col0 + q.ncols > MAK_MAX_COLS ||
-            mak_gemv_lds(q) > (size_t)(q.ncols >= 2 ? kLdsBudgetN : kLdsBudget) || q.n_blocks < 1 ||
+            mak_gemv_lds(q) > (size_t)(q.multi ? kLdsBudgetN : kLdsBudget) || q.n_blocks < 1 ||
             (q.epi == EPI_SWIGLU && (q.geo.r % 2)) ||
-            (q.ncols >= 2 && q.in_kind != IN_RAW && (q.geo.k >> 3) > MAK_NBLOCK))
+            (q.multi && q.in_kind != IN_RAW && (q.geo.k >> 3) > MAK_NBLOCK))
             return fail(MAK_EINVAL, "internal: bad GEMV phase");
         int rc = launch(m, kind, [&](hipEvent_t e0, hipEvent_t e1) { return mak_launch_gemv(q, m->cur, e0, e1); });
         if (rc) return rc;
