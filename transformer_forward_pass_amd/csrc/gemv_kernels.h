@@ -34,7 +34,7 @@ __device__ __forceinline__ int64_t packed_chunk(const PackGeom& g, int64_t row, 
 }
 
 // ---------------------------------------------------------------------------
-// GEMV input staging: hs[c*K + k], bf16, for c < NC (columns >= ncols zero).
+// GEMV input staging: hs[c*K + k] for c < NC (columns >= ncols zero).
 // issue_input() only starts the loads (into registers); finish_input()
 // consumes them.  The weight stream is started in between, and since vector
 // loads retire in order, waiting for the input never waits for the weights.
@@ -78,8 +78,18 @@ __device__ __forceinline__ void issue_input(const GemvPhase& p, Staged<NC>& st, 
     }
 }
 
+// 8 bf16 inputs (one 16-byte chunk) as fp32 (exact) into LDS
+__device__ __forceinline__ void store_chunk_f32(float* dst, uint4 v)
+{
+    float4* d = reinterpret_cast<float4*>(dst);
+    d[0] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+    d[1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
+}
+
+// hs[c*K + k] as fp32 (bf16 values, exact): the fold then converts each
+// input element to fp64 with one instruction
 template <int NC>
-__device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st, uint16_t* hs, double* red,
+__device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st, float* hs, double* red,
                                              const int NT)
 {
     constexpr int QPT = Staged<NC>::QPT;
@@ -87,21 +97,21 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
     const int tid = threadIdx.x;
 #pragma unroll
     for (int c = 0; c < NC; c++) {
-        uint4* h4 = reinterpret_cast<uint4*>(hs + (size_t)c * K);
+        float* hc = hs + (size_t)c * K;
         const int col = p.col0 + c;
         if (c >= p.ncols) {
-            for (int q = tid; q < C; q += NT) h4[q] = make_uint4(0, 0, 0, 0);
+            for (int q = tid; q < C; q += NT) store_chunk_f32(hc + 8 * q, make_uint4(0, 0, 0, 0));
             continue;
         }
         if (p.in_kind == IN_RAW) {
 #pragma unroll
             for (int i = 0; i < QPT; i++) {
                 const int q = tid + i * NT;
-                if (q < C) h4[q] = st.v[c][i];
+                if (q < C) store_chunk_f32(hc + 8 * q, st.v[c][i]);
             }
             // chunks beyond what the registers held (K > QPT*2048)
             const uint4* src = reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
-            for (int q = tid + QPT * NT; q < C; q += NT) h4[q] = src[q];
+            for (int q = tid + QPT * NT; q < C; q += NT) store_chunk_f32(hc + 8 * q, src[q]);
             continue;
         }
         // RMSNorm of x: at most 2 chunks per thread (launches size the
@@ -137,7 +147,7 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
                     const uint32_t hi = rms_apply(bf_hi(u[e]), r, bf_hi(ww[e]));
                     o[e] = lo | (hi << 16);
                 }
-                h4[q] = make_uint4(o[0], o[1], o[2], o[3]);
+                store_chunk_f32(hc + 8 * q, make_uint4(o[0], o[1], o[2], o[3]));
             }
         }
         __syncthreads();  // `red` is reused by the next column
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
     __shared__ float bval[NW][NC];
     __shared__ int bidx[NW][NC];
     __shared__ int is_last;
-    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+    float* hs = reinterpret_cast<float*>(smem);
 
     const int K = p.geo.k;
     const int lane = threadIdx.x & 63;
@@ -347,9 +357,7 @@ __global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
     // 3. fold one completed batch into the accumulators
     auto compute = [&](const uint4 (&buf)[QB], int b) {
         const int n = min(QB, Q - b * QB);
-        uint4 hv[NC];
-        constexpr bool kCacheH = NC <= 2;      // keep the input chunk as fp64
-        double hdc[kCacheH ? NC : 1][8];
+        double hdc[NC][8];
 #pragma unroll
         for (int i = 0; i < QB; i++) {
             if (i < n) {
@@ -358,15 +366,11 @@ __global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
                 if (r == 0) {
                     const int chunk = (((b * QB + i) / RR) << lrl) + s;
 #pragma unroll
-                    for (int c = 0; c < NC; c++)
-                        hv[c] = reinterpret_cast<const uint4*>(hs + (size_t)c * K)[chunk];
-                    if (kCacheH) {
-#pragma unroll
-                        for (int c = 0; c < (kCacheH ? NC : 1); c++) {
-                            const uint32_t hu[4] = {hv[c].x, hv[c].y, hv[c].z, hv[c].w};
-#pragma unroll
-                            for (int e = 0; e < 8; e++) hdc[c][e] = (e & 1) ? bf_hi(hu[e >> 1]) : bf_lo(hu[e >> 1]);
-                        }
+                    for (int c = 0; c < NC; c++) {
+                        const float4* h4 = reinterpret_cast<const float4*>(hs + (size_t)c * K) + 2 * chunk;
+                        const float4 lo = h4[0], hi = h4[1];
+                        hdc[c][0] = lo.x; hdc[c][1] = lo.y; hdc[c][2] = lo.z; hdc[c][3] = lo.w;
+                        hdc[c][4] = hi.x; hdc[c][5] = hi.y; hdc[c][6] = hi.z; hdc[c][7] = hi.w;
                     }
                 }
                 const uint32_t wu[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
@@ -374,16 +378,7 @@ __global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
                 for (int e = 0; e < 8; e++) {
                     const double wd = (e & 1) ? bf_hi(wu[e >> 1]) : bf_lo(wu[e >> 1]);
 #pragma unroll
-                    for (int c = 0; c < NC; c++) {
-                        double hd;
-                        if (kCacheH) {
-                            hd = hdc[kCacheH ? c : 0][e];
-                        } else {
-                            const uint32_t hu = (e < 2) ? hv[c].x : (e < 4) ? hv[c].y : (e < 6) ? hv[c].z : hv[c].w;
-                            hd = (e & 1) ? bf_hi(hu) : bf_lo(hu);
-                        }
-                        acc[r][c] = fma(wd, hd, acc[r][c]);
-                    }
+                    for (int c = 0; c < NC; c++) acc[r][c] = fma(wd, hdc[c][e], acc[r][c]);
                 }
             }
         }
@@ -509,7 +504,7 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
     __shared__ int bidx[NW][1];
     __shared__ int tile_next;
     __shared__ int is_last;
-    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+    float* hs = reinterpret_cast<float*>(smem);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -581,11 +576,9 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
             for (int a = 0; a < A; a++) part[r][a] = 0.0;
 #pragma unroll
         for (int j = 0; j < J; j++) {
-            const uint4 hv = reinterpret_cast<const uint4*>(hs)[(j << lrl) + s];
-            const uint32_t hu[4] = {hv.x, hv.y, hv.z, hv.w};
-            double hd[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) hd[e] = (e & 1) ? bf_hi(hu[e >> 1]) : bf_lo(hu[e >> 1]);
+            const float4* h4 = reinterpret_cast<const float4*>(hs) + 2 * ((j << lrl) + s);
+            const float4 hl = h4[0], hh = h4[1];
+            const double hd[8] = {hl.x, hl.y, hl.z, hl.w, hh.x, hh.y, hh.z, hh.w};
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 const uint4 w = buf[j * R + r];

@@ -361,7 +361,7 @@ size_t mak_gemv_lds(const GemvPhase& p)
 {
     if (p.multi)
         return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.jw, p.geo.lr_log2, p.epi == EPI_SWIGLU);
-    return (size_t)p.geo.k * sizeof(uint16_t);
+    return (size_t)p.geo.k * sizeof(float);
 }
 
 static int device_cus()

@@ -58,7 +58,7 @@ int fail(int code, const char* fmt, ...)
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxGemvBlocks = 1024;      // grid cap of a GEMV phase (waves loop over tiles)
-constexpr int kLdsBudget = 60 * 1024;      // batch-1 GEMV dynamic LDS per workgroup (static LDS < 4 KiB)
+constexpr int kLdsBudget = 96 * 1024;      // batch-1 GEMV dynamic LDS per workgroup (fp32 input row; static < 4 KiB)
 constexpr int kLdsBudgetN = 144 * 1024;    // multi-column GEMV: staged inputs (<= 128 KiB) + partial sums
 constexpr int kLdsInputsN = 128 * 1024;    // multi-column GEMV: NC input rows of K bf16
 constexpr int kAttnLdsBudget = 150 * 1024; // attention dynamic LDS (gfx950: 160 KiB per workgroup)
