@@ -436,7 +436,8 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
     };
 
     // 4. batches ping-pong between two buffers: once one has landed, the
-    //    next is issued and only then is the landed one folded
+    //    next is issued and only then is the landed one folded (a third
+    //    buffer, two batches in flight, was measured slower)
     for (int b = 0; b < n_batches; b += 2) {
         batch_ready<QB>(bufA, QB);
         if (b + 1 < n_batches) issue(bufB);

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 
 #include "device_math.h"
@@ -397,27 +398,127 @@ static int resident_blocks(const void* fn, int threads, size_t lds)
 // Multi-column work split: rows per lane rr (as many as keep >= 1024 tile
 // groups), then waves per group jw (a power of two <= the chunk iterations,
 // within the LDS budget) until about 2048 waves are busy.
-static void gemvn_plan(GemvPhase& p, size_t lds_budget)
+// Work split of a multi-column GEMV: RR rows per lane (rr) and waves per
+// group along K (jw).  Each wave streams its units in batches of QB 16-byte
+// loads per lane (the same bytes for every rr), one batch in flight while it
+// folds the other.  Among the compiled shapes that fit the LDS budget, the
+// plan takes, in this order of priority (measured over the QKV, O, gate/up,
+// down and LM-head matrices of the 135M-1.1B shapes at 8 columns):
+//   1. the fewest rounds of groups (each round ends in a reduce-scatter and
+//      an epilogue that the next round's loads cannot hide: ~2.5 us);
+//   2. the fewest workgroups on the busiest CU (a CU holding two shares the
+//      fp64 arithmetic and the input staging of both);
+//   3. the fewest batches per wave (each is about a memory round trip);
+//   4. the most workgroups (more CUs streaming);
+//   5. rr = 2, then 4, then 1 (rr = 1 converts every input for each row,
+//      rr = 4 holds twice the accumulators);
+//   6. the smallest jw (less LDS combining).
+// MAK_GEMVN_PLAN=0 selects the earlier rule (rr for >= 1024 groups, then jw
+// up to ~2048 waves) for comparison.
+static int gemvn_qb(int nc) { return nc <= 2 ? 16 : nc <= 4 ? 8 : 4; }   // k_gemvn's QB
+
+static void gemvn_plan_auto(GemvPhase& p, size_t lds_budget, int cap);
+
+// Tuning knob: MAK_GEMVN_FORCE="n,k,rr,jw;..." sets (rr, jw) for matrices of
+// n rows by k inputs, when that split is compiled and valid; read at every
+// plan (plans are made when a step is recorded).
+static void gemvn_plan(GemvPhase& p, size_t lds_budget, int cap)
+{
+    gemvn_plan_auto(p, lds_budget, cap);
+    const char* e = getenv("MAK_GEMVN_FORCE");
+    if (!e) return;
+    const int nc = mak_gemv_nc(p.ncols);
+    const int R = p.geo.r, J = (p.geo.k >> 3) >> p.geo.lr_log2;
+    while (*e) {
+        int n = 0, k = 0, rr = 0, jw = 0, used = 0;
+        if (sscanf(e, "%d,%d,%d,%d%n", &n, &k, &rr, &jw, &used) != 4) return;
+        e += used;
+        if (*e == ';') e++;
+        if (n != p.geo.n_rows || k != p.geo.k) continue;
+        const bool ok = (rr == 1 || rr == 2 || rr == 4) && rr >= R && rr % R == 0 && gemvn_fn(rr, nc, p.epi) &&
+                        (jw == 1 || jw == 2 || jw == 4 || jw == 8) && jw <= J && jw <= MAK_NBLOCK / 64 &&
+                        gemvn_lds(nc, p.geo.k, rr, jw, p.geo.lr_log2, p.epi == EPI_SWIGLU) <= lds_budget;
+        if (ok) {
+            p.rr = rr;
+            p.jw = jw;
+        }
+        return;
+    }
+}
+
+static void gemvn_plan_auto(GemvPhase& p, size_t lds_budget, int cap)
 {
     const int nc = mak_gemv_nc(p.ncols);
     const int R = p.geo.r, lrl = p.geo.lr_log2;
     const int J = (p.geo.k >> 3) >> lrl;
     const int64_t tiles = p.geo.n_tiles;
-    int rr = R;
-    for (int cand : {4, 2}) {
-        if (cand < R || cand % R) continue;
-        if ((tiles + cand / R - 1) / (cand / R) >= 1024) {
-            rr = cand;
-            break;
+    const bool pairs = p.epi == EPI_SWIGLU;
+    static int mode = -1;
+    if (mode < 0) {
+        const char* e = getenv("MAK_GEMVN_PLAN");
+        mode = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    if (mode == 0) {
+        int rr = R;
+        for (int cand : {4, 2}) {
+            if (cand < R || cand % R) continue;
+            if ((tiles + cand / R - 1) / (cand / R) >= 1024) {
+                rr = cand;
+                break;
+            }
+        }
+        const int64_t ng = (tiles + rr / R - 1) / (rr / R);
+        int jw = 1;
+        while (jw * 2 <= MAK_NBLOCK / 64 && jw * 2 <= J && ng * jw < 2048 &&
+               gemvn_lds(nc, p.geo.k, rr, jw * 2, lrl, pairs) <= lds_budget)
+            jw *= 2;
+        p.rr = rr;
+        p.jw = jw;
+        return;
+    }
+    const int n_cu = device_cus();
+    const int qb = gemvn_qb(nc);
+    const int nw = MAK_NBLOCK / 64;
+    auto rr_rank = [](int rr) { return rr == 2 ? 0 : rr == 4 ? 1 : 2; };
+    bool have = false;
+    int64_t b_rounds = 0, b_per_cu = 0, b_batches = 0, b_blocks = 0;
+    int b_rank = 0, b_jw = 0;
+    p.rr = R;
+    p.jw = 1;
+    for (int rr : {4, 2, 1}) {
+        if (rr < R || rr % R) continue;
+        const void* fn = gemvn_fn(rr, nc, p.epi);
+        if (!fn) continue;
+        const int ub = std::max(1, qb / rr);
+        const int64_t ng = (tiles + rr / R - 1) / (rr / R);
+        for (int jw = 1; jw <= nw && jw <= J; jw *= 2) {
+            const size_t lds = gemvn_lds(nc, p.geo.k, rr, jw, lrl, pairs);
+            if (lds > lds_budget) break;
+            const int occ = resident_blocks(fn, MAK_NBLOCK, lds);
+            const int64_t gpr = nw / jw;
+            const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((ng + gpr - 1) / gpr, std::min(occ * n_cu, cap)));
+            const int64_t rounds = (ng + blocks * gpr - 1) / (blocks * gpr);
+            const int64_t per_cu = (blocks + n_cu - 1) / n_cu;
+            const int64_t batches = (rounds * ((J + jw - 1) / jw) + ub - 1) / ub;
+            const int rank = rr_rank(rr);
+            bool better = !have;
+            if (have) {
+                if (rounds != b_rounds) better = rounds < b_rounds;
+                else if (per_cu != b_per_cu) better = per_cu < b_per_cu;
+                else if (batches != b_batches) better = batches < b_batches;
+                else if (blocks != b_blocks) better = blocks > b_blocks;
+                else if (rank != b_rank) better = rank < b_rank;
+                else better = jw < b_jw;
+            }
+            if (better) {
+                have = true;
+                b_rounds = rounds, b_per_cu = per_cu, b_batches = batches, b_blocks = blocks;
+                b_rank = rank, b_jw = jw;
+                p.rr = rr;
+                p.jw = jw;
+            }
         }
     }
-    const int64_t ng = (tiles + rr / R - 1) / (rr / R);
-    int jw = 1;
-    while (jw * 2 <= MAK_NBLOCK / 64 && jw * 2 <= J && ng * jw < 2048 &&
-           gemvn_lds(nc, p.geo.k, rr, jw * 2, lrl, p.epi == EPI_SWIGLU) <= lds_budget)
-        jw *= 2;
-    p.rr = rr;
-    p.jw = jw;
 }
 
 // Grid of a GEMV phase.  Batch-1: one wave per tile while that fits on the
@@ -432,7 +533,7 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
     // measured slower: its staging and combine cost more than the fold)
     p.multi = p.ncols >= 2;
     if (p.multi) {
-        gemvn_plan(p, lds_budget_n);
+        gemvn_plan(p, lds_budget_n, cap);
         p.threads = MAK_NBLOCK;
         const void* fn = gemv_fn(p);
         if (!fn) return 0;
