@@ -104,6 +104,14 @@ def _attn_bytes(shape, p0, n_new, chunk=8):
     return total * shape.n_layers, steps * shape.n_layers
 
 
+_T_START = time.perf_counter()
+
+
+def progress(msg):
+    """One stderr line per finished section (long counter-collection runs)."""
+    print("[bench %.1fs] %s" % (time.perf_counter() - _T_START, msg), file=sys.stderr, flush=True)
+
+
 def run_gpu(args, shape, wl, w, prompt, steps):
     import torch
     from transformer_forward_pass_amd import mak
@@ -112,11 +120,13 @@ def run_gpu(args, shape, wl, w, prompt, steps):
     for _ in range(args.warmup):
         m.generate(prompt, max_new)
     torch.cuda.synchronize()
+    progress("%s: warmup done" % shape.name)
     t0 = time.perf_counter()
     for _ in range(steps):
         m.generate(prompt, max_new)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    progress("%s: timed steps done" % shape.name)
 
     # the prompt alone (chunked prefill + LM head), timed the same way, to
     # separate the steady-state decode rate
@@ -126,6 +136,7 @@ def run_gpu(args, shape, wl, w, prompt, steps):
         m.prefill(prompt, want_logits=True)
     torch.cuda.synchronize()
     t_prefill = (time.perf_counter() - t1) / steps
+    progress("%s: prefill timing done" % shape.name)
 
     # second pass with per-launch HIP events on the model's stream
     m.set_phase_timing(True)
@@ -134,6 +145,7 @@ def run_gpu(args, shape, wl, w, prompt, steps):
     times = m.phase_times()
     m.set_phase_timing(False)
     m.free()
+    progress("%s: phase timing done" % shape.name)
     return dt, t_prefill, times
 
 
@@ -343,7 +355,9 @@ def main():
                             "phase_ms_per_step": r2["phase_ms_per_step"]}
     if not args.no_extra and not args.max_new:
         out["batched"] = measure_batched(args)
+        progress("batched decode done")
         out["long_context"] = measure_long(args)
+        progress("long-context run done")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(r["shape"], r["w"], r["prompt"], args.cpu_new)
     print(json.dumps(out))
