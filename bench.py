@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -121,9 +122,13 @@ def run_gpu(args, shape, wl, w, prompt, steps):
         m.generate(prompt, max_new)
     torch.cuda.synchronize()
     progress("%s: warmup done" % shape.name)
+    # each step timed on its own as well (median and min of the runs)
+    runs = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        m.generate(prompt, max_new)
+        t_run = time.perf_counter()
+        m.generate(prompt, max_new)   # returns after its device-to-host token copy
+        runs.append(time.perf_counter() - t_run)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     progress("%s: timed steps done" % shape.name)
@@ -146,7 +151,7 @@ def run_gpu(args, shape, wl, w, prompt, steps):
     m.set_phase_timing(False)
     m.free()
     progress("%s: phase timing done" % shape.name)
-    return dt, t_prefill, times
+    return dt, t_prefill, times, runs
 
 
 def measure(args, name, steps):
@@ -159,7 +164,7 @@ def measure(args, name, steps):
     shape = wl.shape
     w = synth.make_weights(shape)
     prompt = synth.make_prompts(wl)[0]
-    dt, t_prefill, times = run_gpu(args, shape, wl, w, prompt, steps)
+    dt, t_prefill, times, runs = run_gpu(args, shape, wl, w, prompt, steps)
     p0, n = len(prompt), wl.max_new
     t_decode = (dt / steps - t_prefill) / (n - 1)
     kinds = [k for k in ("qkv", "attn", "o", "gateup", "down", "lmhead") if times[k][1]]
@@ -177,6 +182,8 @@ def measure(args, name, steps):
     return {
         "shape": shape, "w": w, "prompt": prompt, "wl": wl,
         "tok_s": n * steps / dt, "ms_per_step": 1e3 * dt / steps,
+        "runs_ms": {"median": round(1e3 * statistics.median(runs), 4), "min": round(1e3 * min(runs), 4),
+                    "n": len(runs)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "bytes_per_launch": per_launch,
@@ -344,6 +351,7 @@ def main():
         "roofline": r["roofline"],
         "token_roofline": r["token_roofline"],
         "phase_ms_per_step": r["phase_ms_per_step"],
+        "runs_ms": r["runs_ms"],
     }
     if not args.no_secondary:
         r2 = measure(args, SECONDARY, max(2, args.steps // 2))
@@ -352,7 +360,7 @@ def main():
                             "value": round(r2["tok_s"], 2), "unit": "tok/s",
                             "ms_per_step": round(r2["ms_per_step"], 4),
                             "roofline": r2["roofline"], "token_roofline": r2["token_roofline"],
-                            "phase_ms_per_step": r2["phase_ms_per_step"]}
+                            "phase_ms_per_step": r2["phase_ms_per_step"], "runs_ms": r2["runs_ms"]}
     if not args.no_extra and not args.max_new:
         out["batched"] = measure_batched(args)
         progress("batched decode done")
