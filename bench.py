@@ -208,10 +208,10 @@ def cpu_baseline(shape, w, prompt, n_new):
 
 
 def measure_batched(args, name="tinyllama-1.1b", reps=2):
-    """Batched decode (8 sequences with their own slots and positions, one
-    multi-column step per token): aggregate tok/s over 127 steps after each
-    sequence's prompt is prefilled, plus per-phase times and the dominant
-    GEMV's roofline over a timed pass of 16 steps."""
+    """Batched decode (8 or 16 sequences with their own slots and positions,
+    one multi-column step per token): aggregate tok/s over 127 steps after
+    each sequence's prompt is prefilled, plus per-phase times and the
+    dominant GEMV's roofline over a timed pass of 16 steps."""
     import torch
     from transformer_forward_pass_amd import mak, synth
     wl = synth.WORKLOADS[name]
@@ -364,6 +364,8 @@ def main():
     if not args.no_extra and not args.max_new:
         out["batched"] = measure_batched(args)
         progress("batched decode done")
+        out["batched16"] = measure_batched(args, "tinyllama-1.1b-b16")
+        progress("16-sequence batched decode done")
         out["long_context"] = measure_long(args)
         progress("long-context run done")
     if not args.no_cpu:

@@ -46,7 +46,7 @@ extern "C" {
 #define MAK_ENOMEM (-3)   /* arena smaller than mak_plan's figure                   */
 #define MAK_EDEVICE (-4)  /* HIP runtime error (message kept for mak_last_error)     */
 
-#define MAK_MAX_BATCH 8     /* columns of one decode batch                          */
+#define MAK_MAX_BATCH 16    /* columns of one decode batch                          */
 #define MAK_PREFILL_CHUNK 8 /* prompts are consumed in chunks of at most 8 tokens    */
 
 /* Model shape.  head_dim a power of two in [16, 128]; hidden, intermediate and

@@ -47,7 +47,7 @@ def test_plan_sizes_arena_without_gpu():
 
 
 @pytest.mark.parametrize("field,value", [("hidden", 100), ("head_dim", 48), ("n_kv_heads", 5),
-                                         ("max_batch", 9), ("vocab", 0), ("max_seq", 0)])
+                                         ("max_batch", 17), ("vocab", 0), ("max_seq", 0)])
 def test_plan_rejects_bad_shapes(field, value):
     import dataclasses
     s = dataclasses.replace(synth.SHAPES["tiny"], **{field: value})

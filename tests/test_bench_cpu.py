@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_workloads_named_by_bench_exist():
-    for name in (bench.WORKLOAD, bench.SECONDARY, "tinyllama-1.1b", "qwen3-0.6b"):
+    for name in (bench.WORKLOAD, bench.SECONDARY, "tinyllama-1.1b", "tinyllama-1.1b-b16", "qwen3-0.6b"):
         assert name in synth.WORKLOADS
 
 

@@ -1,0 +1,70 @@
+"""Batched decode beyond 8 columns: up to 16 sequences advance together, the
+weights streamed once per step for all of them ("model-as-a-kernel", API:
+decode_batch).  Each sequence's tokens and logits must equal decoding it
+alone (the one-column kernels) bitwise, and match the CPU oracle.  Covers
+full (16) and padded (9, 13) column groups (each wave of the GEMVs stages
+two columns' RMSNorm rows), permuted slots, head_dim 64 and 32, GQA."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from tests.parity import logits_ok
+from transformer_forward_pass_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny-d64": dataclasses.replace(synth.SHAPES["tiny"], max_batch=16),
+    "d32-gqa3": synth.small_shape(n_layers=2, hidden=192, n_q_heads=6, n_kv_heads=2, head_dim=32,
+                                  intermediate=344, vocab=1000, max_batch=16),
+}
+STEPS = 3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    return torch
+
+
+def _np(t):
+    return t.double().cpu().numpy()
+
+
+def _prompts(shape, n, seed=7):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(3, 21, n)
+    return [[int(t) for t in rng.integers(0, shape.vocab, int(k))] for k in lens]
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+@pytest.mark.parametrize("B", [16, 13, 9])
+def test_batch_up_to_16_equals_alone_and_oracle(torch_cuda, orc, name, B):
+    from transformer_forward_pass_amd import mak
+    s = SHAPES[name]
+    w = synth.make_weights(s)
+    prompts = _prompts(s, B)
+    slots = list(range(B))[::-1] if B == 13 else list(range(B))   # permuted slots once
+    bat = mak.MakModel(s, w, max_seq=64, max_batch=16)
+    one = mak.MakModel(s, w, max_seq=64, max_batch=16)
+    for b, p in enumerate(prompts):
+        bat.prefill(p, slot=slots[b], want_logits=False)
+        one.prefill(p, slot=slots[b], want_logits=False)
+    toks = [(37 * b + 11) % s.vocab for b in range(B)]
+    pos = [len(p) for p in prompts]
+    out, lg = bat.decode_batch(toks, pos, slots=slots, steps=STEPS)
+    lg = _np(lg)
+    for b in range(B):
+        o1, l1 = one.decode_batch([toks[b]], [pos[b]], slots=[slots[b]], steps=STEPS)
+        assert np.array_equal(out[:, b], o1[:, 0]), "%s B=%d column %d tokens" % (name, B, b)
+        assert np.array_equal(lg[b], _np(l1)[0]), "%s B=%d column %d logits" % (name, B, b)
+    for b in (0, B - 1):
+        o = orc.Oracle(s, w, max_len=64)
+        o.prefill(prompts[b])
+        t = toks[b]
+        for st in range(STEPS):
+            ref = o.decode_step(t, pos[b] + st)
+            t = int(out[st, b])
+        logits_ok(lg[b], ref, "%s B=%d column %d" % (name, B, b))

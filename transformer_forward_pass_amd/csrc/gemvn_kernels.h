@@ -28,19 +28,23 @@ __device__ __forceinline__ uint4 keep_or_zero(bool keep, uint4 a)
     return make_uint4(keep ? a.x : 0u, keep ? a.y : 0u, keep ? a.z : 0u, keep ? a.w : 0u);
 }
 
-// Input staging.  RMSNorm inputs (K <= 4096): wave c stages column c, each
-// lane holding chunks lane + 64*i, so a column's sum of squares is one wave
-// reduction and no barrier separates the statistics from the normalisation.
-// Raw inputs: a plain copy spread over all threads.
+// Input staging.  RMSNorm inputs (K <= 4096): wave w stages columns w,
+// w + 8, ... (at most two), each lane holding chunks lane + 64*i, so a
+// column's sum of squares is one wave reduction and no barrier separates
+// the statistics from the normalisation.  Raw inputs: a plain copy spread
+// over all threads.
 constexpr int kStageChunks = 8;   // chunks per lane for RMSNorm inputs (K <= 64*8*8)
+constexpr int kStageWaves = MAK_NBLOCK / 64;
 
+template <int NC>
 struct StagedN {
-    uint4 v[kStageChunks];
-    uint4 w[kStageChunks];
+    static constexpr int CR = (NC + kStageWaves - 1) / kStageWaves;   // columns per wave
+    uint4 v[CR][kStageChunks];
+    uint4 w[kStageChunks];   // the norm weight, the same for every column
 };
 
 template <int NC>
-__device__ __forceinline__ void issue_inputs_n(const GemvPhase& p, StagedN& st)
+__device__ __forceinline__ void issue_inputs_n(const GemvPhase& p, StagedN<NC>& st)
 {
     if (p.in_kind == IN_RAW) return;
     const int C = p.geo.k >> 3;
@@ -48,25 +52,32 @@ __device__ __forceinline__ void issue_inputs_n(const GemvPhase& p, StagedN& st)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave >= NC) return;
     const int n_i = (C + 63) >> 6;
-    const int col = p.col0 + min(wave, p.ncols - 1);
     const bool gather = p.in_kind == IN_GATHER_NORM;
-    const uint4* base = gather ? reinterpret_cast<const uint4*>(p.embed)
-                               : reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
-    const int token = gather ? p.ctl->cols[col].token : 0;
     const uint4* nw = reinterpret_cast<const uint4*>(p.norm_w);
 #pragma unroll
-    for (int i = 0; i < kStageChunks; i++) {
-        if (i < n_i) {
-            const int q = min(lane + 64 * i, C - 1);
-            st.v[i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
-            st.w[i] = nw[q];
+    for (int r = 0; r < StagedN<NC>::CR; r++) {
+        const int cw = wave + r * kStageWaves;
+        if (cw >= NC) continue;   // wave-uniform
+        const int col = p.col0 + min(cw, p.ncols - 1);
+        const uint4* base = gather ? reinterpret_cast<const uint4*>(p.embed)
+                                   : reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
+        const int token = gather ? p.ctl->cols[col].token : 0;
+#pragma unroll
+        for (int i = 0; i < kStageChunks; i++) {
+            if (i < n_i) {
+                const int q = min(lane + 64 * i, C - 1);
+                st.v[r][i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
+            }
         }
     }
+#pragma unroll
+    for (int i = 0; i < kStageChunks; i++)
+        if (i < n_i) st.w[i] = nw[min(lane + 64 * i, C - 1)];
 }
 
 // hs[c*K + k] (bf16) for c < NC; columns >= ncols are zero.
 template <int NC>
-__device__ __forceinline__ void finish_inputs_n(const GemvPhase& p, const StagedN& st, uint16_t* hs)
+__device__ __forceinline__ void finish_inputs_n(const GemvPhase& p, const StagedN<NC>& st, uint16_t* hs)
 {
     const int K = p.geo.k, C = K >> 3;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -93,39 +104,44 @@ __device__ __forceinline__ void finish_inputs_n(const GemvPhase& p, const Staged
     }
     if (wave >= NC) return;
     const int n_i = (C + 63) >> 6;
-    const bool active = wave < p.ncols;
-    double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < kStageChunks; i++) {
-        if (i < n_i && lane + 64 * i < C) {
-            const uint32_t u[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
+    for (int r = 0; r < StagedN<NC>::CR; r++) {
+        const int cw = wave + r * kStageWaves;   // this wave's r-th column
+        if (cw >= NC) continue;                  // wave-uniform
+        const bool active = cw < p.ncols;
+        double ss = 0.0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const double a = bf_lo(u[e]), b = bf_hi(u[e]);
-                ss = fma(a, a, ss);
-                ss = fma(b, b, ss);
+        for (int i = 0; i < kStageChunks; i++) {
+            if (i < n_i && lane + 64 * i < C) {
+                const uint32_t u[4] = {st.v[r][i].x, st.v[r][i].y, st.v[r][i].z, st.v[r][i].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const double a = bf_lo(u[e]), b = bf_hi(u[e]);
+                    ss = fma(a, a, ss);
+                    ss = fma(b, b, ss);
+                }
             }
         }
-    }
-    ss = wave_sum(ss);
-    const float r = rms_scale(ss, K, p.eps);
-    const bool store_x = active && p.in_kind == IN_GATHER_NORM && blockIdx.x == 0;
-    uint4* xs = reinterpret_cast<uint4*>(p.x_store + (size_t)(p.col0 + wave) * p.x_ld);
+        ss = wave_sum(ss);
+        const float rs = rms_scale(ss, K, p.eps);
+        const bool store_x = active && p.in_kind == IN_GATHER_NORM && blockIdx.x == 0;
+        uint4* xs = reinterpret_cast<uint4*>(p.x_store + (size_t)(p.col0 + cw) * p.x_ld);
 #pragma unroll
-    for (int i = 0; i < kStageChunks; i++) {
-        const int q = lane + 64 * i;
-        if (i < n_i && q < C) {
-            if (store_x) xs[q] = st.v[i];
-            const uint32_t u[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
-            const uint32_t ww[4] = {st.w[i].x, st.w[i].y, st.w[i].z, st.w[i].w};
-            uint32_t o[4];
+        for (int i = 0; i < kStageChunks; i++) {
+            const int q = lane + 64 * i;
+            if (i < n_i && q < C) {
+                if (store_x) xs[q] = st.v[r][i];
+                const uint32_t u[4] = {st.v[r][i].x, st.v[r][i].y, st.v[r][i].z, st.v[r][i].w};
+                const uint32_t ww[4] = {st.w[i].x, st.w[i].y, st.w[i].z, st.w[i].w};
+                uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t lo = rms_apply(bf_lo(u[e]), r, bf_lo(ww[e]));
-                const uint32_t hi = rms_apply(bf_hi(u[e]), r, bf_hi(ww[e]));
-                o[e] = lo | (hi << 16);
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t lo = rms_apply(bf_lo(u[e]), rs, bf_lo(ww[e]));
+                    const uint32_t hi = rms_apply(bf_hi(u[e]), rs, bf_hi(ww[e]));
+                    o[e] = lo | (hi << 16);
+                }
+                hs4[cw * C + q] = keep_or_zero(active, make_uint4(o[0], o[1], o[2], o[3]));
             }
-            hs4[wave * C + q] = keep_or_zero(active, make_uint4(o[0], o[1], o[2], o[3]));
         }
     }
 }
@@ -225,6 +241,7 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
     constexpr int LOGV = (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
     constexpr int HM = (EPI == EPI_SWIGLU) ? LOGV - 1 : LOGV;   // halvings at most
     constexpr int QB = (NC <= 2) ? 16 : (NC <= 4) ? 8 : 4;   // 16-byte loads per lane per batch
+    static_assert(RR * NC <= 32, "the reduce-scatter handles at most 32 values per lane");
     constexpr int UB = (QB / RR) > 0 ? QB / RR : 1;        // units per batch
     static_assert(UB * RR == QB, "batch must hold whole units");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -289,7 +306,7 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
     };
 
     // 1. input loads, the first weight batch, then the staged (normalised) inputs
-    StagedN st;
+    StagedN<NC> st;
     issue_inputs_n<NC>(p, st);
     uint4 bufA[QB], bufB[QB];
     const int n_batches = (total + UB - 1) / UB;
@@ -454,8 +471,9 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
 }  // namespace mak
 
 // rows per lane (RR) x column capacity (NC) instantiated for the multi-column GEMV
-#define MAK_GEMVN_SHAPES(X) X(1, 2) X(2, 2) X(4, 2) X(1, 4) X(2, 4) X(4, 4) X(1, 8) X(2, 8) X(4, 8)
-#define MAK_GEMVN_PAIR_SHAPES(X) X(2, 2) X(4, 2) X(2, 4) X(4, 4) X(2, 8) X(4, 8)
+#define MAK_GEMVN_SHAPES(X) \
+    X(1, 2) X(2, 2) X(4, 2) X(1, 4) X(2, 4) X(4, 4) X(1, 8) X(2, 8) X(4, 8) X(1, 16) X(2, 16)
+#define MAK_GEMVN_PAIR_SHAPES(X) X(2, 2) X(4, 2) X(2, 4) X(4, 4) X(2, 8) X(4, 8) X(2, 16)
 
 // defined in gemvn_*.hip: the kernel for (rr, nc), or nullptr
 const void* mak_gemvn_fn_store(int rr, int nc);

@@ -317,7 +317,7 @@ static const void* gemv_fn_r1(int epi)
 }
 
 // Column capacity (template NC) for n active columns.
-int mak_gemv_nc(int ncols) { return ncols <= 1 ? 1 : ncols <= 2 ? 2 : ncols <= 4 ? 4 : 8; }
+int mak_gemv_nc(int ncols) { return ncols <= 1 ? 1 : ncols <= 2 ? 2 : ncols <= 4 ? 4 : ncols <= 8 ? 8 : 16; }
 
 static const void* gemvn_fn(int rr, int nc, int epi)
 {
@@ -650,7 +650,7 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
             const void* f = (r == 1) ? gemv_fn_r1<1>(epi) : (r == 2) ? gemv_fn_r1<2>(epi) : gemv_fn_r1<4>(epi);
             hipError_t e = set(f, bytes);
             if (e != hipSuccess) return e;
-            for (int nc : {2, 4, 8}) {
+            for (int nc : {2, 4, 8, 16}) {
                 e = set(gemvn_fn(r, nc, epi), bytes_n);
                 if (e != hipSuccess) return e;
             }

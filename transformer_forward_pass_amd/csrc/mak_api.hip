@@ -343,6 +343,7 @@ int collect_timing(mak_model* m)
 int max_cols_for_k(int k)
 {
     int n = kLdsInputsN / (k * 2);
+    if (n >= 16) return 16;
     if (n >= 8) return 8;
     if (n >= 4) return 4;
     if (n >= 2) return 2;

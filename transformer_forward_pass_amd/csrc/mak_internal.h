@@ -8,7 +8,7 @@
 #define MAK_BLOCK 256               // threads per workgroup (4 waves)
 #define MAK_GBLOCK 512              // threads per workgroup of the batch-1 GEMV (8 waves, one workgroup per CU)
 #define MAK_NBLOCK 512              // threads per workgroup of the multi-column GEMV (8 waves)
-#define MAK_MAX_COLS 8              // columns (batch rows / prefill tokens) per step
+#define MAK_MAX_COLS 16             // columns per step (batch rows; prefill chunks use <= 8)
 #define MAK_ATTN_CHUNK 128          // positions per chunk of the split-KV attention
 
 // ---------------------------------------------------------------------------

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmak.so")
 
 MAK_OK, MAK_EINVAL, MAK_ERANGE, MAK_ENOMEM, MAK_EDEVICE = 0, -1, -2, -3, -4
-MAK_MAX_BATCH = 8
+MAK_MAX_BATCH = 16
 MAK_PREFILL_CHUNK = 8
 
 EXPORTS = ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_generate",

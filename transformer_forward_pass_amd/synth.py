@@ -111,6 +111,9 @@ WORKLOADS: Dict[str, Workload] = {
     "qwen3-0.6b": Workload(SHAPES["qwen3-0.6b"], prompt_len=512, max_new=256),
     "tinyllama-1.1b": Workload(SHAPES["tinyllama-1.1b"], prompt_len=16, max_new=128,
                                batch=8, prompt_len_hi=256),
+    # the same shape and weights, 16 sequences decoded together
+    "tinyllama-1.1b-b16": Workload(dataclasses.replace(SHAPES["tinyllama-1.1b"], max_batch=16),
+                                   prompt_len=16, max_new=128, batch=16, prompt_len_hi=256),
 }
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
