@@ -1,5 +1,5 @@
 // gemvn_kernels.h -- the multi-column GEMV of prefill chunks and batched
-// decode (gfx950): y[c] = W x[c] for up to 8 columns, the weights streamed
+// decode (gfx950): y[c] = W x[c] for up to 16 columns, the weights streamed
 // once for all of them.
 //
 // Same packed weight layout and the same fp64 arithmetic as the batch-1
