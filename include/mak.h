@@ -100,8 +100,9 @@ int mak_load(const mak_config *cfg, const mak_weights *w, void *d_arena, size_t 
              void *hip_stream, mak_model **out);
 
 /* Consume n prompt tokens of sequence `slot` at positions start_pos ..
- * start_pos+n-1, in chunks of at most MAK_PREFILL_CHUNK ("model-as-a-kernel",
- * Usage: chunked prompt consumption).  start_pos may not exceed the slot's
+ * start_pos+n-1, in chunks of at most MAK_PREFILL_CHUNK tokens, or the size
+ * set by mak_set_prefill_chunk ("model-as-a-kernel", Usage: chunked prompt
+ * consumption).  start_pos may not exceed the slot's
  * cached length.  If d_logits is not NULL it receives the fp32 logits [vocab]
  * of the last prompt token.  n >= 1. */
 int mak_prefill(mak_model *m, int32_t slot, const int32_t *ids, int32_t n, int32_t start_pos,
@@ -161,6 +162,14 @@ int mak_set_executor(mak_model *m, int executor);
  * the chunk sums in chunk order.  Both forms give bitwise-identical results;
  * 0 always splits.  Returns MAK_EINVAL for a negative threshold. */
 int mak_set_attention_split(mak_model *m, int32_t above);
+
+/* Prompt tokens per prefill step, 1..16 (default MAK_PREFILL_CHUNK = 8).  The
+ * "model-as-a-kernel" page consumes prompts in chunks of up to eight tokens,
+ * bitwise identical to token-by-token consumption (Method section).  Larger
+ * chunks stream each layer's weights once for more tokens and stay bitwise
+ * identical, since every dot product is exact before its single rounding.
+ * Returns MAK_EINVAL outside 1..16. */
+int mak_set_prefill_chunk(mak_model *m, int32_t tokens);
 
 /* Per-phase timing ("model-as-a-kernel", API: decode_step_timed runs the
  * phases one launch each and reports per-phase milliseconds).  While

@@ -1,4 +1,4 @@
-"""Batched decode beyond 8 columns: up to 16 sequences advance together, the
+"""Steps of more than 8 columns.  Batched decode: up to 16 sequences advance together, the
 weights streamed once per step for all of them ("model-as-a-kernel", API:
 decode_batch).  Each sequence's tokens and logits must equal decoding it
 alone (the one-column kernels) bitwise, and match the CPU oracle.  Covers
@@ -68,3 +68,46 @@ def test_batch_up_to_16_equals_alone_and_oracle(torch_cuda, orc, name, B):
             ref = o.decode_step(t, pos[b] + st)
             t = int(out[st, b])
         logits_ok(lg[b], ref, "%s B=%d column %d" % (name, B, b))
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_prefill_chunk_16_equals_8_and_token_by_token(torch_cuda, orc, name):
+    """A 37-token prompt in chunks of 16 (16, 16, 5), 8 and 1: last-token
+    logits and the KV cache bitwise equal, and within tolerance of the oracle."""
+    from transformer_forward_pass_amd import mak
+    s = SHAPES[name]
+    w = synth.make_weights(s)
+    ids = [int(t) for t in np.random.default_rng(3).integers(0, s.vocab, 37)]
+    runs = []
+    for chunk in (16, 8, 1):
+        m = mak.MakModel(s, w, max_seq=64)
+        m.set_prefill_chunk(chunk)
+        lg = _np(m.prefill(ids))
+        kv = [m.read_kv(l, 0, 0, len(ids)) for l in range(s.n_layers)]
+        runs.append((lg, kv))
+    for lg, kv in runs[1:]:
+        assert np.array_equal(runs[0][0], lg), name + " logits: chunk 16 != chunk 8 / 1"
+        for l in range(s.n_layers):
+            assert np.array_equal(runs[0][1][l][0], kv[l][0]) and np.array_equal(runs[0][1][l][1], kv[l][1])
+    logits_ok(runs[0][0], orc.Oracle(s, w, max_len=64).prefill(ids), name + " chunk 16")
+
+
+def test_prefill_chunk_16_through_split_attention(torch_cuda):
+    """300 tokens in chunks of 16 with split-KV attention from the first chunk
+    equal chunks of 8 with single-pass attention, bitwise."""
+    from transformer_forward_pass_amd import mak
+    s = SHAPES["tiny-d64"]
+    w = synth.make_weights(s)
+    ids = [int(t) for t in np.random.default_rng(5).integers(0, s.vocab, 300)]
+    a = mak.MakModel(s, w, max_seq=512)
+    a.set_prefill_chunk(16)
+    a.set_attention_split(0)
+    b = mak.MakModel(s, w, max_seq=512)
+    b.set_attention_split(1 << 30)
+    assert np.array_equal(_np(a.prefill(ids)), _np(b.prefill(ids)))
+    for l in range(s.n_layers):
+        ka, va = a.read_kv(l, 0, 0, 300)
+        kb, vb = b.read_kv(l, 0, 0, 300)
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    with pytest.raises(mak.MakError):
+        a.set_prefill_chunk(17)

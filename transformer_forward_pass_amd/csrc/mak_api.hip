@@ -283,6 +283,7 @@ struct mak_model {
     hipStream_t cur = nullptr;       // stream the phase launches go to (capture or model stream)
     hipStream_t capture = nullptr;   // private stream used only to capture step graphs
     bool use_graphs = true;
+    int prefill_chunk = MAK_PREFILL_CHUNK;   // prompt tokens per prefill step (<= MAK_MAX_COLS)
     int split_above = 0;                 // split-KV attention once pos + 1 exceeds this
     std::vector<StepGraph> graphs;
     Layout L;
@@ -567,8 +568,8 @@ int set_cols(mak_model* m, const ColState* cols, int ncols, int step)
 int prefill_chunks(mak_model* m, int slot, const int32_t* ids, int n, int start_pos, bool want_lm,
                    int step0)
 {
-    for (int c0 = 0; c0 < n; c0 += MAK_PREFILL_CHUNK) {
-        const int T = std::min(MAK_PREFILL_CHUNK, n - c0);
+    for (int c0 = 0; c0 < n; c0 += m->prefill_chunk) {
+        const int T = std::min(m->prefill_chunk, n - c0);
         ColState cols[MAK_MAX_COLS] = {};
         for (int t = 0; t < T; t++) {
             cols[t].token = ids[c0 + t];
@@ -760,6 +761,15 @@ int mak_set_attention_split(mak_model* m, int32_t above)
     if (rc) return rc;
     if (above < 0) return fail(MAK_EINVAL, "split threshold %d < 0", above);
     m->split_above = above;
+    return MAK_OK;
+}
+
+int mak_set_prefill_chunk(mak_model* m, int32_t tokens)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    if (tokens < 1 || tokens > MAK_MAX_COLS) return fail(MAK_EINVAL, "prefill chunk %d not in [1, %d]", tokens, MAK_MAX_COLS);
+    m->prefill_chunk = tokens;
     return MAK_OK;
 }
 
