@@ -67,12 +67,10 @@ __device__ __forceinline__ void issue_inputs_n(const GemvPhase& p, StagedN<NC>& 
             if (i < n_i) {
                 const int q = min(lane + 64 * i, C - 1);
                 st.v[r][i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
+                if (r == 0) st.w[i] = nw[q];   // the norm weight, with the first column
             }
         }
     }
-#pragma unroll
-    for (int i = 0; i < kStageChunks; i++)
-        if (i < n_i) st.w[i] = nw[min(lane + 64 * i, C - 1)];
 }
 
 // hs[c*K + k] (bf16) for c < NC; columns >= ncols are zero.
