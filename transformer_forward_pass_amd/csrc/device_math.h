@@ -196,6 +196,30 @@ __device__ __forceinline__ double block_sum_rt(double v, double* red, int nw)
     return s;
 }
 
+// Workgroup barrier that orders LDS only: global loads still in flight stay
+// in flight (a plain __syncthreads also fences global memory, so the
+// compiler first drains every outstanding vector load).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// block_sum_rt with LDS-only barriers (a GEMV's input statistics, while its
+// first weight batch is still arriving)
+__device__ __forceinline__ double block_sum_lds(double v, double* red, int nw)
+{
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    lds_barrier();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    lds_barrier();
+    double s = red[0];
+    for (int i = 1; i < nw; i++) s += red[i];
+    return s;
+}
+
 __device__ __forceinline__ float block_max(float v, float* red)
 {
     v = wave_max(v);

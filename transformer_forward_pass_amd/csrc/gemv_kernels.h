@@ -132,7 +132,7 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
                 }
             }
         }
-        ss = block_sum_rt(ss, red, NT >> 6);
+        ss = block_sum_lds(ss, red, NT >> 6);
         const float r = rms_scale(ss, K, p.eps);
 #pragma unroll
         for (int i = 0; i < 2; i++) {
@@ -150,7 +150,7 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
                 store_chunk_f32(hc + 8 * q, make_uint4(o[0], o[1], o[2], o[3]));
             }
         }
-        __syncthreads();  // `red` is reused by the next column
+        lds_barrier();  // `red` is reused by the next column
     }
 }
 
@@ -520,10 +520,15 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
     const char* W = reinterpret_cast<const char*>(p.w);
     const uint32_t lane_off = (uint32_t)lane * 16u;
 
+    // (issued in chunk order: an empty asm with a memory clobber keeps the
+    // compiler from reordering them, so chunk i's wait leaves QT-1-i in flight)
     auto issue = [&](uint4 (&buf)[QT], int t) {
         const char* wt = W + (int64_t)t * QT * 1024;
 #pragma unroll
-        for (int i = 0; i < QT; i++) buf[i] = *reinterpret_cast<const uint4*>(wt + lane_off + i * 1024);
+        for (int i = 0; i < QT; i++) {
+            buf[i] = *reinterpret_cast<const uint4*>(wt + lane_off + i * 1024);
+            asm volatile("" ::: "memory");
+        }
     };
 
     // Tiles.  With at most one tile per wave: tile = global wave index.
@@ -555,13 +560,17 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
     };
     uint4 bufA[QT], bufB[QT];
     // the first weight batch is issued before the input is staged, so both
-    // arrive in one round trip and the stream starts at once
-    if (tile < t_end) {
-        load_res(tile);
-        issue(bufA, tile);
+    // arrive in one round trip and the stream starts at once.  Unconditional
+    // (a wave without a tile loads the last one and drops it): loads issued
+    // on every path keep the compiler's wait counts exact, so the fold
+    // below waits for each chunk's loads only.
+    {
+        const int t0 = min(tile, n_tiles - 1);
+        load_res(t0);
+        issue(bufA, t0);
     }
     finish_input<1>(p, stg, hs, red, nw * 64);
-    __syncthreads();   // also publishes tile_next
+    lds_barrier();   // publishes the staged input and tile_next (LDS only: the weights keep arriving)
 
     float best_v = -INFINITY;
     int best_i = 0x7fffffff;
@@ -579,9 +588,18 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
             const float4* h4 = reinterpret_cast<const float4*>(hs) + 2 * ((j << lrl) + s);
             const float4 hl = h4[0], hh = h4[1];
             const double hd[8] = {hl.x, hl.y, hl.z, hl.w, hh.x, hh.y, hh.z, hh.w};
+            // Fold the chunks in load order, each waiting only for its own
+            // load: empty asms that may rewrite the accumulators (so chunk
+            // j's FMAs stay after chunk j-1's) and the chunk (so its uses stay
+            // after that point).
+#pragma unroll
+            for (int r = 0; r < R; r++)
+#pragma unroll
+                for (int a = 0; a < A; a++) asm volatile("" : "+v"(part[r][a]));
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const uint4 w = buf[j * R + r];
+                uint4 w = buf[j * R + r];
+                asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
                 const uint32_t wu[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                 for (int e = 0; e < 8; e++)
@@ -632,20 +650,28 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
         }
     };
 
-    while (tile < t_end) {
-        int nt = next_tile(tile);
-        batch_ready<QT>(bufA, QT);
-        if (nt < t_end) issue(bufB, nt);
-        fold(bufA, tile);
-        if (nt < t_end) load_res(nt);
-        tile = nt;
-        if (tile >= t_end) break;
-        nt = next_tile(tile);
-        batch_ready<QT>(bufB, QT);
-        if (nt < t_end) issue(bufA, nt);
-        fold(bufB, tile);
-        if (nt < t_end) load_res(nt);
-        tile = nt;
+    if (!dyn) {
+        // at most one tile per wave: fold it straight after staging, outside
+        // any loop, so that each chunk iteration waits only for its own loads
+        // (straight-line code gets per-load wait counts) and the arithmetic
+        // of the first chunks overlaps the arrival of the last
+        if (tile < t_end) fold(bufA, tile);
+    } else {
+        while (tile < t_end) {
+            int nt = next_tile(tile);
+            batch_ready<QT>(bufA, QT);
+            if (nt < t_end) issue(bufB, nt);
+            fold(bufA, tile);
+            if (nt < t_end) load_res(nt);
+            tile = nt;
+            if (tile >= t_end) break;
+            nt = next_tile(tile);
+            batch_ready<QT>(bufB, QT);
+            if (nt < t_end) issue(bufA, nt);
+            fold(bufB, tile);
+            if (nt < t_end) load_res(nt);
+            tile = nt;
+        }
     }
     if (EPI == EPI_LOGITS) argmax_tail<1>(p, &best_v, &best_i, bval, bidx, is_last, lane, wave, nw);
 }
