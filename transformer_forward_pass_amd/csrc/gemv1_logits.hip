@@ -3,10 +3,10 @@
 
 using namespace mak;
 
-const void* mak_gemv1_fn_logits(int r, int j)
+const void* mak_gemv1_fn_logits(int r, int j, int ks)
 {
 #define X(R, J) \
-    if (r == R && j == J) return reinterpret_cast<const void*>(&k_gemv1<R, J, EPI_LOGITS>);
+    if (ks == 1 && r == R && j == J) return reinterpret_cast<const void*>(&k_gemv1<R, J, EPI_LOGITS>);
     MAK_GEMV1_SHAPES(X)
 #undef X
     return nullptr;

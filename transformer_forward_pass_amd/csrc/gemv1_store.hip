@@ -3,11 +3,15 @@
 
 using namespace mak;
 
-const void* mak_gemv1_fn_store(int r, int j)
+const void* mak_gemv1_fn_store(int r, int j, int ks)
 {
 #define X(R, J) \
-    if (r == R && j == J) return reinterpret_cast<const void*>(&k_gemv1<R, J, EPI_STORE>);
+    if (ks == 1 && r == R && j == J) return reinterpret_cast<const void*>(&k_gemv1<R, J, EPI_STORE>);
     MAK_GEMV1_SHAPES(X)
+#undef X
+#define X(R, J) \
+    if (ks == 2 && r == R && j == J) return reinterpret_cast<const void*>(&k_gemv1<R, J, EPI_STORE, 2>);
+    MAK_GEMV1_KS_SHAPES(X)
 #undef X
     return nullptr;
 }

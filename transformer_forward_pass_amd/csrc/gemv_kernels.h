@@ -493,10 +493,19 @@ __global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
 // J*R loads need more registers than two waves per SIMD leave.
 __host__ __device__ constexpr int gemv1_waves(int r, int j) { return r * j > 16 ? 4 : 8; }
 
-template <int R, int J, int EPI>
+// KS = 2 splits each tile's chunks over two waves (static path only: at
+// most one tile per pair of waves): waves 2m and 2m+1 fold the first and
+// second half of tile m's chunks, and the second hands its row sums to the
+// first through LDS, which adds them (first half + second half) and applies
+// the epilogue.  For odd J both halves issue the same number of loads (the
+// second repeats the last chunk and skips it) so the waits stay exact.
+template <int R, int J, int EPI, int KS = 1>
 __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
 {
+    static_assert(KS == 1 || KS == 2, "K split of 1 or 2");
     constexpr int QT = J * R;
+    constexpr int JH = (J + KS - 1) / KS;                  // chunk iterations per wave
+    constexpr int QH = JH * R;                             // loads per wave per tile
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int NW = gemv1_waves(R, J);
     __shared__ double red[NW];
@@ -522,11 +531,15 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
 
     // (issued in chunk order: an empty asm with a memory clobber keeps the
     // compiler from reordering them, so chunk i's wait leaves QT-1-i in flight)
+    // (KS = 2: this wave's half of the chunks, the last repeated for odd J)
+    const int half = (KS == 2) ? (wave & 1) : 0;
     auto issue = [&](uint4 (&buf)[QT], int t) {
         const char* wt = W + (int64_t)t * QT * 1024;
 #pragma unroll
-        for (int i = 0; i < QT; i++) {
-            buf[i] = *reinterpret_cast<const uint4*>(wt + lane_off + i * 1024);
+        for (int i = 0; i < QH; i++) {
+            const int c = i / R;
+            const int jj = (KS == 2) ? min(half * JH + c, J - 1) : c;
+            buf[i] = *reinterpret_cast<const uint4*>(wt + lane_off + (jj * R + (i - c * R)) * 1024);
             asm volatile("" ::: "memory");
         }
     };
@@ -536,10 +549,10 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
     // take them one at a time from an LDS counter, so waves that get more
     // of the CU's memory bandwidth do more tiles and all finish together
     // (which tile a wave computes does not change any result).
-    const bool dyn = n_tiles > n_waves;
+    const bool dyn = KS == 1 && n_tiles > n_waves;            // (KS = 2: the host launches >= 2 waves per tile)
     const int t_begin = dyn ? (int)((int64_t)blockIdx.x * n_tiles / gridDim.x) : 0;
     const int t_end = dyn ? (int)((int64_t)(blockIdx.x + 1) * n_tiles / gridDim.x) : n_tiles;
-    int tile = dyn ? t_begin + wave : blockIdx.x * nw + wave;   // dyn: each range holds >= nw tiles
+    int tile = dyn ? t_begin + wave : (blockIdx.x * nw + wave) / KS;   // dyn: each range holds >= nw tiles
     if (threadIdx.x == 0) tile_next = t_begin + nw;
     auto next_tile = [&](int t) __attribute__((always_inline)) {
         if (!dyn) return t + n_waves;
@@ -577,14 +590,18 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
 
     // independent partial sums per row (4 chains in flight per lane)
     constexpr int A = (R >= 4) ? 1 : 4 / R;
-    auto fold = [&](const uint4 (&buf)[QT], int t) {
+    // row sums of this wave's chunks of a tile: chunk c of the batch is
+    // chunk j0 + c of the tile (n of them)
+    auto dot = [&](const uint4 (&buf)[QT], double (&acc)[R], int j0, int n) __attribute__((always_inline)) {
         double part[R][A];
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
             for (int a = 0; a < A; a++) part[r][a] = 0.0;
 #pragma unroll
-        for (int j = 0; j < J; j++) {
+        for (int c = 0; c < JH; c++) {
+            if (c >= n) break;   // (wave-uniform: only the second half of an odd J)
+            const int j = j0 + c;
             const float4* h4 = reinterpret_cast<const float4*>(hs) + 2 * ((j << lrl) + s);
             const float4 hl = h4[0], hh = h4[1];
             const double hd[8] = {hl.x, hl.y, hl.z, hl.w, hh.x, hh.y, hh.z, hh.w};
@@ -598,7 +615,7 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
                 for (int a = 0; a < A; a++) asm volatile("" : "+v"(part[r][a]));
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                uint4 w = buf[j * R + r];
+                uint4 w = buf[c * R + r];
                 asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
                 const uint32_t wu[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -607,7 +624,6 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
                                          part[r][e % A]);
             }
         }
-        double acc[R];
 #pragma unroll
         for (int r = 0; r < R; r++) {
             acc[r] = part[r][0];
@@ -615,6 +631,9 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
             for (int a = 1; a < A; a++) acc[r] += part[r][a];
             acc[r] = group_sum_rt(acc[r], lrl);
         }
+    };
+    // epilogue of tile t from its row sums (lanes with s == 0)
+    auto emit = [&](const double (&acc)[R], int t) __attribute__((always_inline)) {
         if (s != 0) return;
         const int row0 = t * G * R + grp * R;
         const size_t col = (size_t)p.col0;
@@ -650,13 +669,39 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
         }
     };
 
+    auto fold = [&](const uint4 (&buf)[QT], int t) __attribute__((always_inline)) {
+        double acc[R];
+        dot(buf, acc, 0, J);
+        emit(acc, t);
+    };
+
     if (!dyn) {
         // at most one tile per wave: fold it straight after staging, outside
         // any loop, so that each chunk iteration waits only for its own loads
         // (straight-line code gets per-load wait counts) and the arithmetic
         // of the first chunks overlaps the arrival of the last
-        if (tile < t_end) fold(bufA, tile);
-    } else {
+        if constexpr (KS == 1) {
+            if (tile < t_end) fold(bufA, tile);
+        } else {
+            // (waves without a tile fold their repeated data and drop it, so
+            // every wave reaches the barrier)
+            __shared__ double xch[4][64][R];
+            double acc[R];
+            dot(bufA, acc, half * JH, half ? J - JH : JH);
+            if (half == 1 && s == 0) {
+#pragma unroll
+                for (int r = 0; r < R; r++) xch[wave >> 1][grp][r] = acc[r];
+            }
+            lds_barrier();
+            if (half == 0 && tile < t_end) {
+                if (s == 0) {
+#pragma unroll
+                    for (int r = 0; r < R; r++) acc[r] += xch[wave >> 1][grp][r];
+                }
+                emit(acc, tile);
+            }
+        }
+    } else if constexpr (KS == 1) {
         while (tile < t_end) {
             int nt = next_tile(tile);
             batch_ready<QT>(bufA, QT);
@@ -685,9 +730,14 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
     X(1, 6) X(2, 6) X(1, 9) X(2, 9) X(1, 11) X(1, 16)
 // gate/up pairs need an even R
 #define MAK_GEMV1_PAIR_SHAPES(X) X(2, 1) X(4, 1) X(2, 2) X(4, 2) X(2, 3) X(4, 3) X(2, 4) X(4, 4) X(2, 6) X(2, 9)
+// shapes that also have a K-split (KS = 2) kernel: three or more chunk iterations
+#define MAK_GEMV1_KS_SHAPES(X) \
+    X(1, 3) X(2, 3) X(4, 3) X(1, 4) X(2, 4) X(4, 4) X(1, 6) X(2, 6) X(1, 9) X(2, 9) X(1, 11) X(1, 16)
+#define MAK_GEMV1_KS_PAIR_SHAPES(X) X(2, 3) X(4, 3) X(2, 4) X(4, 4) X(2, 6) X(2, 9)
 
-// defined in gemv1_*.hip: the compiled kernel for (r, j), or nullptr
-const void* mak_gemv1_fn_store(int r, int j);
-const void* mak_gemv1_fn_residual(int r, int j);
-const void* mak_gemv1_fn_swiglu(int r, int j);
-const void* mak_gemv1_fn_logits(int r, int j);
+// defined in gemv1_*.hip: the compiled kernel for (r, j) and K split ks (1
+// or 2), or nullptr
+const void* mak_gemv1_fn_store(int r, int j, int ks = 1);
+const void* mak_gemv1_fn_residual(int r, int j, int ks = 1);
+const void* mak_gemv1_fn_swiglu(int r, int j, int ks = 1);
+const void* mak_gemv1_fn_logits(int r, int j, int ks = 1);

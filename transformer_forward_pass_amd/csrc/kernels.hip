@@ -330,19 +330,21 @@ static const void* gemvn_fn(int rr, int nc, int epi)
     return nullptr;
 }
 
-static const void* gemv1_fn(const GemvPhase& p)
+static const void* gemv1_fn_ks(const GemvPhase& p, int ks)
 {
     const int j = (p.geo.k >> 3) >> p.geo.lr_log2;
     switch (p.epi) {
-    case EPI_STORE: return mak_gemv1_fn_store(p.geo.r, j);
-    case EPI_RESIDUAL: return mak_gemv1_fn_residual(p.geo.r, j);
-    case EPI_SWIGLU: return mak_gemv1_fn_swiglu(p.geo.r, j);
-    case EPI_LOGITS: return mak_gemv1_fn_logits(p.geo.r, j);
+    case EPI_STORE: return mak_gemv1_fn_store(p.geo.r, j, ks);
+    case EPI_RESIDUAL: return mak_gemv1_fn_residual(p.geo.r, j, ks);
+    case EPI_SWIGLU: return mak_gemv1_fn_swiglu(p.geo.r, j, ks);
+    case EPI_LOGITS: return mak_gemv1_fn_logits(p.geo.r, j, ks);
     }
     return nullptr;
 }
 
-static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn(p) != nullptr; }
+static const void* gemv1_fn(const GemvPhase& p) { return gemv1_fn_ks(p, p.ks == 2 ? 2 : 1); }
+
+static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn_ks(p, 1) != nullptr; }
 
 static const void* gemv_fn(const GemvPhase& p)
 {
@@ -556,6 +558,7 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
         per_cu = (e && atoi(e) > 0) ? atoi(e) : 1;
     }
     const int64_t tiles = p.geo.n_tiles;
+    p.ks = 1;
     if (!gemv1_compiled(p)) {
         p.threads = MAK_GBLOCK;
         const int wpb = MAK_GBLOCK / 64;
@@ -570,11 +573,27 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             const char* e = getenv("MAK_GEMV_STATIC_WAVES");
             sw = (e && (atoi(e) == 1 || atoi(e) == 2 || atoi(e) == 4)) ? atoi(e) : 0;
         }
+        // K split: with room for two waves per tile, each folds half of the
+        // tile's chunks (MAK_GEMV_KSPLIT=0 turns it off)
+        static int ks_env = -1;
+        if (ks_env < 0) {
+            const char* e = getenv("MAK_GEMV_KSPLIT");
+            ks_env = (e && atoi(e) == 0) ? 0 : 1;
+        }
+        const int64_t waves1 = tiles;
+        int w = sw ? sw : (waves1 <= 1024 ? 2 : 4);
+        if (ks_env && 2 * tiles <= 8 * (int64_t)n_cu && w >= 2 && gemv1_fn_ks(p, 2)) p.ks = 2;
+        const int64_t waves = tiles * p.ks;
+        if (!sw) w = waves <= 1024 ? 2 : 4;
         // RMSNorm staging holds 2 chunks of 8 inputs per thread
-        int w = sw ? sw : (tiles <= 1024 ? 2 : 4);
         while (p.in_kind != IN_RAW && w < 4 && 64 * w * 16 < p.geo.k) w *= 2;
         p.threads = 64 * w;
-        return (int)std::min<int64_t>((tiles + w - 1) / w, cap);
+        const int64_t blocks = (waves + w - 1) / w;
+        if (p.ks == 2 && blocks > cap) {   // (the K-split kernel has no tile loop: every tile needs its pair)
+            p.ks = 1;
+            return (int)std::min<int64_t>((tiles + w - 1) / w, cap);
+        }
+        return (int)std::min<int64_t>(blocks, cap);
     }
     const int j = (p.geo.k >> 3) >> p.geo.lr_log2;
     p.threads = gemv1_waves(p.geo.r, j) * 64;
@@ -657,11 +676,12 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
         }
     for (int r : {1, 2, 4})
         for (int j : {1, 2, 3, 4, 6, 9, 11, 16})
-            for (const void* f : {mak_gemv1_fn_store(r, j), mak_gemv1_fn_residual(r, j), mak_gemv1_fn_swiglu(r, j),
-                                  mak_gemv1_fn_logits(r, j)}) {
-                hipError_t e = set(f, bytes);
-                if (e != hipSuccess) return e;
-            }
+            for (int ks : {1, 2})
+                for (const void* f : {mak_gemv1_fn_store(r, j, ks), mak_gemv1_fn_residual(r, j, ks),
+                                      mak_gemv1_fn_swiglu(r, j, ks), mak_gemv1_fn_logits(r, j, ks)}) {
+                    hipError_t e = set(f, bytes);
+                    if (e != hipSuccess) return e;
+                }
 #define X(D)                                                                               \
     {                                                                                      \
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D>),       \

@@ -93,6 +93,7 @@ struct GemvPhase {
     int32_t jw;               // multi-column kernel: waves sharing one tile group (split of K)
     int32_t threads;          // workgroup size of the launch
     int32_t multi;            // 1: the multi-column kernel (k_gemvn) runs the launch
+    int32_t ks;               // batch-1 kernel: waves per tile (1, or 2 = chunks split over a wave pair)
     float* part_val;          // EPI_LOGITS per-block partial maxima [n_blocks][MAK_MAX_COLS]
     int32_t* part_idx;
     int32_t* out_tokens;      // EPI_LOGITS: emitted tokens [step][lm_count] (device)
