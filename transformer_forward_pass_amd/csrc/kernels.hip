@@ -30,6 +30,9 @@
 
 namespace mak {
 
+constexpr int kAttnWaves = 8;                       // waves per attention workgroup
+constexpr int kAttnBlock = kAttnWaves * 64;
+
 // ---------------------------------------------------------------------------
 // attention: one workgroup per (column, query head)
 // ---------------------------------------------------------------------------
@@ -42,12 +45,14 @@ namespace mak {
 // cache row another one writes in the same launch.
 //
 // Lanes split a K/V row into 16-byte chunks (LP = d/8 lanes per row); rows
-// spread over lane groups and the 4 waves; each lane keeps U rows in flight.
+// spread over lane groups and the kAttnWaves waves (two per SIMD, so one
+// wave's dependent steps overlap the other's); each lane keeps U rows in
+// flight.
 //
-// LDS (dynamic): pv[16][d] f64 | qf[d] f32 | kin[8][d] bf16 | vin[8][d] bf16 |
+// LDS (dynamic): pv[4 * kAttnWaves][d] f64 | qf[d] f32 | kin[8][d] bf16 | vin[8][d] bf16 |
 //                rope cos, sin [9][d/2] bf16 | S[max_seq] f32
 template <int D_>
-__global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
+__global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int d = D_ > 0 ? D_ : p.head_dim;
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     double* pv = reinterpret_cast<double*>(smem);
-    float* qf = reinterpret_cast<float*>(pv + 16 * d);
+    float* qf = reinterpret_cast<float*>(pv + 4 * kAttnWaves * d);
     uint16_t* kin = reinterpret_cast<uint16_t*>(qf + d);
     uint16_t* vin = kin + MAK_MAX_COLS * d;
     uint16_t* rc = vin + MAK_MAX_COLS * d;            // rope rows: 0 = pos, 1 + ci = fp + ci
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
     const int lp_log2 = __builtin_ctz(d >> 3);
     const int LP = 1 << lp_log2;
     const int rows_w = 64 >> lp_log2;
-    const int rows_it = 4 * rows_w;
+    const int rows_it = kAttnWaves * rows_w;
     const int sub = lane >> lp_log2, ch = lane & (LP - 1);
     const int my_row = wave * rows_w + sub;
     constexpr int U = 8;   // rows per lane per pass: 256 positions per round trip at d = 64
@@ -97,14 +102,14 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
             vpre[u] = *reinterpret_cast<const uint4*>(vc_h + (size_t)j * d + ch * 8);
         }
     }
-    for (int t = tid; t < d; t += MAK_BLOCK) qf[t] = bf2f(p.qkv[(size_t)col * p.qkv_ld + h * d + t]);
-    for (int t = tid; t < n_in * d; t += MAK_BLOCK) {
+    for (int t = tid; t < d; t += kAttnBlock) qf[t] = bf2f(p.qkv[(size_t)col * p.qkv_ld + h * d + t]);
+    for (int t = tid; t < n_in * d; t += kAttnBlock) {
         const int ci = t / d, i = t - ci * d;
         const size_t base = (size_t)(cs.first_col + ci) * p.qkv_ld;
         kin[t] = p.qkv[base + q_dim + g * d + i];
         vin[t] = p.qkv[base + q_dim + kv_dim + g * d + i];
     }
-    for (int t = tid; t < (1 + n_in) * half; t += MAK_BLOCK) {
+    for (int t = tid; t < (1 + n_in) * half; t += kAttnBlock) {
         const int ri = t / half, i = t - ri * half;
         const int at = (ri == 0) ? pos : fp + ri - 1;
         rc[t] = p.cos_t[(size_t)at * half + i];
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
 
     // per-head qk RMSNorm (one wave per vector: q, then the step's k rows)
     if (p.q_norm) {
-        for (int vi = wave; vi < 1 + n_in; vi += 4) {
+        for (int vi = wave; vi < 1 + n_in; vi += kAttnWaves) {
             double ss = 0.0;
             for (int i = lane; i < d; i += 64) {
                 const double x = (vi == 0) ? (double)qf[i] : (double)bf2f(kin[(vi - 1) * d + i]);
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
     }
 
     // rope (pairs i, i + d/2): q at pos, the step's k rows at fp + ci
-    for (int t = tid; t < (1 + n_in) * half; t += MAK_BLOCK) {
+    for (int t = tid; t < (1 + n_in) * half; t += kAttnBlock) {
         const int vi = t / half, i = t - vi * half;
         const float c = bf2f(rc[vi * half + i]);
         const float sn = bf2f(rsn[vi * half + i]);
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
 
     // append this column's k', v at pos (single owner per kv group)
     if (owner) {
-        for (int i = tid; i < d; i += MAK_BLOCK) {
+        for (int i = tid; i < d; i += kAttnBlock) {
             p.kc[(head_base + pos) * d + i] = kin[(n_in - 1) * d + i];
             p.vc[(head_base + pos) * d + i] = vin[(n_in - 1) * d + i];
         }
@@ -208,23 +213,23 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
             for (int j = lane; j < n; j += 64) S[j] = rbf((float)((double)S[j] / Z));
         }
     } else {
-        __shared__ float redf[MAK_BLOCK / 64];
-        __shared__ double redd[MAK_BLOCK / 64];
+        __shared__ float redf[kAttnBlock / 64];
+        __shared__ double redd[kAttnBlock / 64];
         float m = -INFINITY;
-        for (int j = tid; j < n; j += MAK_BLOCK) m = fmaxf(m, S[j]);
+        for (int j = tid; j < n; j += kAttnBlock) m = fmaxf(m, S[j]);
         m = wave_max(m);
         if (lane == 0) redf[wave] = m;
         __syncthreads();
         m = redf[0];
-        for (int w = 1; w < MAK_BLOCK / 64; w++) m = fmaxf(m, redf[w]);
+        for (int w = 1; w < kAttnBlock / 64; w++) m = fmaxf(m, redf[w]);
         double z = 0.0;
-        for (int j = tid; j < n; j += MAK_BLOCK) {
+        for (int j = tid; j < n; j += kAttnBlock) {
             const float e = (float)exp((double)S[j] - (double)m);
             S[j] = e;
             z += (double)e;
         }
-        const double Z = (double)(float)block_sum_rt(z, redd, MAK_BLOCK / 64);
-        for (int j = tid; j < n; j += MAK_BLOCK) S[j] = rbf((float)((double)S[j] / Z));
+        const double Z = (double)(float)block_sum_rt(z, redd, kAttnBlock / 64);
+        for (int j = tid; j < n; j += kAttnBlock) S[j] = rbf((float)((double)S[j] / Z));
     }
     __syncthreads();
 
@@ -269,10 +274,10 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn(AttnPhase p)
         for (int e = 0; e < 8; e++) pv[grp16 * d + ch * 8 + e] = acc[e];
     }
     __syncthreads();
-    for (int i = tid; i < d; i += MAK_BLOCK) {
+    for (int i = tid; i < d; i += kAttnBlock) {
         double v = 0.0;
 #pragma unroll
-        for (int gi = 0; gi < 16; gi++) v += pv[gi * d + i];
+        for (int gi = 0; gi < 4 * kAttnWaves; gi++) v += pv[gi * d + i];
         p.o[(size_t)col * q_dim + h * d + i] = f2bf((float)v);
     }
 }
@@ -617,12 +622,12 @@ hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hi
     return launch_fn(gemv_fn(p), dim3(p.n_blocks), dim3(gemv_threads(p)), args, mak_gemv_lds(p), st, e0, e1);
 }
 
-// dynamic LDS of k_attn: pv[16][d] f64 | qf[d] f32 | kin, vin [8][d] bf16 |
+// dynamic LDS of k_attn: pv[4 * kAttnWaves][d] f64 | qf[d] f32 | kin, vin [8][d] bf16 |
 // rope [9][d/2] bf16 x 2 | S[s_cap] f32
 size_t mak_attn_lds_for(int rep, int d, int max_seq)
 {
     (void)rep;
-    return (size_t)16 * d * 8 + (size_t)d * 4 + 2 * (size_t)MAK_MAX_COLS * d * 2 +
+    return (size_t)4 * kAttnWaves * d * 8 + (size_t)d * 4 + 2 * (size_t)MAK_MAX_COLS * d * 2 +
            2 * (size_t)(MAK_MAX_COLS + 1) * (d / 2) * 2 + (size_t)max_seq * 4;
 }
 
@@ -642,7 +647,7 @@ hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hi
 #undef X
     AttnPhase q = p;
     void* args[] = {&q};
-    return launch_fn(fn, dim3(p.ncols * p.n_q_heads), dim3(MAK_BLOCK), args, mak_attn_lds(p), st, e0, e1);
+    return launch_fn(fn, dim3(p.ncols * p.n_q_heads), dim3(kAttnBlock), args, mak_attn_lds(p), st, e0, e1);
 }
 
 hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st, hipEvent_t e0,
