@@ -578,16 +578,21 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             const char* e = getenv("MAK_GEMV_STATIC_WAVES");
             sw = (e && (atoi(e) == 1 || atoi(e) == 2 || atoi(e) == 4)) ? atoi(e) : 0;
         }
-        // K split: with room for two waves per tile, each folds half of the
-        // tile's chunks (MAK_GEMV_KSPLIT=0 turns it off)
-        static int ks_env = -1;
+        // K split: with room for two waves per tile (up to ks_wpc waves per
+        // CU: 16, measured faster than 8 on the 1B shape's O and down GEMVs,
+        // whose 4096 waves no longer fit at once), each folds half of the
+        // tile's chunks (MAK_GEMV_KSPLIT=0 turns it off; MAK_GEMV_KSPLIT_WPC
+        // sets the waves per CU)
+        static int ks_env = -1, ks_wpc = 16;
         if (ks_env < 0) {
             const char* e = getenv("MAK_GEMV_KSPLIT");
             ks_env = (e && atoi(e) == 0) ? 0 : 1;
+            const char* e2 = getenv("MAK_GEMV_KSPLIT_WPC");
+            if (e2 && atoi(e2) >= 2 && atoi(e2) <= 32) ks_wpc = atoi(e2);
         }
         const int64_t waves1 = tiles;
         int w = sw ? sw : (waves1 <= 1024 ? 2 : 4);
-        if (ks_env && 2 * tiles <= 8 * (int64_t)n_cu && w >= 2 && gemv1_fn_ks(p, 2)) p.ks = 2;
+        if (ks_env && 2 * tiles <= (int64_t)ks_wpc * n_cu && w >= 2 && gemv1_fn_ks(p, 2)) p.ks = 2;
         const int64_t waves = tiles * p.ks;
         if (!sw) w = waves <= 1024 ? 2 : 4;
         // RMSNorm staging holds 2 chunks of 8 inputs per thread
