@@ -34,7 +34,7 @@ __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 // ---------------------------------------------------------------------------
 // Cross-lane moves.  DPP lane moves are VALU instructions (a few cycles)
 // where __shfl_xor goes through the LDS crossbar (ds_bpermute, ~100 cycles),
-// so reductions use DPP inside a 16-lane row and the crossbar only between
+// so reductions use DPP inside a 16-lane row and the row-swap moves between
 // rows.  64-bit values move as two 32-bit halves.
 // ---------------------------------------------------------------------------
 enum : int {
@@ -60,6 +60,58 @@ __device__ __forceinline__ float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// Across rows: gfx950's row-swap moves (v_permlane16_swap, v_permlane32_swap;
+// VALU, no LDS crossbar).  With both operands equal, every lane receives the
+// value of the lower and of the upper lane of its pair (lane, lane ^ 16) or
+// (lane, lane ^ 32), in that order, so both lanes compute the same
+// lower-plus-upper sum (equal to v + partner: addition commutes).
+template <int DIST>
+__device__ __forceinline__ void xor_pair_d(double v, double& lower, double& upper)
+{
+    static_assert(DIST == 16 || DIST == 32, "row-swap distances");
+    const unsigned lo = (unsigned)__double2loint(v), hi = (unsigned)__double2hiint(v);
+    if (DIST == 16) {
+        const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+        const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+        lower = __hiloint2double((int)h[0], (int)l[0]);
+        upper = __hiloint2double((int)h[1], (int)l[1]);
+    } else {
+        const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        lower = __hiloint2double((int)h[0], (int)l[0]);
+        upper = __hiloint2double((int)h[1], (int)l[1]);
+    }
+}
+
+// v + (v at lane ^ DIST)
+template <int DIST>
+__device__ __forceinline__ double add_xor(double v)
+{
+    double a, b;
+    xor_pair_d<DIST>(v, a, b);
+    return a + b;
+}
+
+// v at lane ^ DIST
+template <int DIST>
+__device__ __forceinline__ double get_xor(double v)
+{
+    double a, b;
+    xor_pair_d<DIST>(v, a, b);
+    return (threadIdx.x & DIST) ? a : b;
+}
+
+// max(v, v at lane ^ DIST)
+template <int DIST>
+__device__ __forceinline__ float max_xor(float v)
+{
+    static_assert(DIST == 16 || DIST == 32, "row-swap distances");
+    const unsigned u = __float_as_uint(v);
+    const auto p = (DIST == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // Sum over aligned groups of 2^LOG lanes (LOG <= 6); every lane of a group
 // gets the group's sum (the same tree in every group).
 template <int LOG>
@@ -69,8 +121,8 @@ __device__ __forceinline__ double group_sum(double v)
     if (LOG >= 2) v += dpp_d<DPP_XOR2>(v);
     if (LOG >= 3) v += dpp_d<DPP_HALF_MIRROR>(v);
     if (LOG >= 4) v += dpp_d<DPP_MIRROR>(v);
-    if (LOG >= 5) v += __shfl_xor(v, 16, 64);
-    if (LOG >= 6) v += __shfl_xor(v, 32, 64);
+    if (LOG >= 5) v = add_xor<16>(v);
+    if (LOG >= 6) v = add_xor<32>(v);
     return v;
 }
 
@@ -81,8 +133,8 @@ __device__ __forceinline__ double group_sum_rt(double v, int log)
     if (log >= 2) v += dpp_d<DPP_XOR2>(v);
     if (log >= 3) v += dpp_d<DPP_HALF_MIRROR>(v);
     if (log >= 4) v += dpp_d<DPP_MIRROR>(v);
-    if (log >= 5) v += __shfl_xor(v, 16, 64);
-    if (log >= 6) v += __shfl_xor(v, 32, 64);
+    if (log >= 5) v = add_xor<16>(v);
+    if (log >= 6) v = add_xor<32>(v);
     return v;
 }
 
@@ -108,18 +160,12 @@ __device__ __forceinline__ void group_sum_all(double (&v)[N], int log)
         for (int i = 0; i < N; i++) v[i] += dpp_d<DPP_MIRROR>(v[i]);
     }
     if (log >= 5) {
-        double t[N];
 #pragma unroll
-        for (int i = 0; i < N; i++) t[i] = __shfl_xor(v[i], 16, 64);
-#pragma unroll
-        for (int i = 0; i < N; i++) v[i] += t[i];
+        for (int i = 0; i < N; i++) v[i] = add_xor<16>(v[i]);
     }
     if (log >= 6) {
-        double t[N];
 #pragma unroll
-        for (int i = 0; i < N; i++) t[i] = __shfl_xor(v[i], 32, 64);
-#pragma unroll
-        for (int i = 0; i < N; i++) v[i] += t[i];
+        for (int i = 0; i < N; i++) v[i] = add_xor<32>(v[i]);
     }
 }
 
@@ -130,8 +176,8 @@ __device__ __forceinline__ float group_max(float v)
     if (LOG >= 2) v = fmaxf(v, dpp_f<DPP_XOR2>(v));
     if (LOG >= 3) v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
     if (LOG >= 4) v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
-    if (LOG >= 5) v = fmaxf(v, __shfl_xor(v, 16, 64));
-    if (LOG >= 6) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    if (LOG >= 5) v = max_xor<16>(v);
+    if (LOG >= 6) v = max_xor<32>(v);
     return v;
 }
 
@@ -145,8 +191,8 @@ __device__ __forceinline__ double stride_sum(double v)
     if (LOG <= 1) v += dpp_d<0x122>(v);   // row_ror:2
     if (LOG <= 2) v += dpp_d<DPP_ROR4>(v);
     if (LOG <= 3) v += dpp_d<DPP_ROR8>(v);
-    if (LOG <= 4) v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    if (LOG <= 4) v = add_xor<16>(v);
+    v = add_xor<32>(v);
     return v;
 }
 

@@ -184,7 +184,8 @@ __device__ __forceinline__ double xor_lanes(double v)
         const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(v), 0x101F);
         return __hiloint2double(hi, lo);
     }
-    return __shfl_xor(v, 1 << K, 64);
+    if (K == 4) return get_xor<16>(v);
+    return get_xor<32>(v);
 }
 
 // Reduce-scatter of a[0..V) over the 2^lrl lanes of each row group, lane
