@@ -562,6 +562,14 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
     };
     Staged<1> stg;
     issue_input<1>(p, stg, nw * 64);
+    // every wave's input loads go out before any weight load of the
+    // workgroup, so the input and its RMSNorm do not queue behind the CU's
+    // first weight batches (a barrier without a fence: nothing waits for
+    // the loads here; the empty asms keep the compiler from moving loads
+    // across it)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     float xres[R];
     auto load_res = [&](int t) {
         if (EPI == EPI_RESIDUAL && s == 0) {
