@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
     const int rows_it = kAttnWaves * rows_w;
     const int sub = lane >> lp_log2, ch = lane & (LP - 1);
     const int my_row = wave * rows_w + sub;
-    constexpr int U = 8;   // rows per lane per pass: 256 positions per round trip at d = 64
+    constexpr int U = 8;   // rows per lane per pass: 512 positions per round trip at d = 64
 
     // ---- round trip 1: this column's state
     const ColState cs = p.ctl->cols[col];
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
     __syncthreads();
 
     // o = bf16(sum_j P_j V_j): per-lane partial sums over its rows, folded
-    // within each 16-lane row (DPP), then the 16 rows of the block through LDS
+    // within each 16-lane row (DPP), then the block's 4 * kAttnWaves rows through LDS
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[e] = 0.0;
