@@ -569,7 +569,21 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
         const int wpb = MAK_GBLOCK / 64;
         return (int)std::max<int64_t>(1, std::min<int64_t>((tiles + wpb - 1) / wpb, std::min(per_cu * n_cu, cap)));
     }
-    if (tiles <= 8 * (int64_t)n_cu) {
+    // One tile per wave up to wpc waves per CU, beyond that the tile queue.
+    // All such waves need not be resident at once (the static path has no
+    // cross-workgroup waits): 32 waves per CU measured faster than 8 for the
+    // 1B shape's QKV and gate/up GEMVs (1166 -> 1195 tok/s), but slower for
+    // the LM head, which keeps 8 (MAK_GEMV_STATIC_WPC overrides the 32).
+    // The grid cap rises to 4096 workgroups except for the LM head, whose
+    // per-workgroup argmax partials are sized for `cap`.
+    static int static_wpc = -1;
+    if (static_wpc < 0) {
+        const char* e = getenv("MAK_GEMV_STATIC_WPC");
+        static_wpc = (e && atoi(e) >= 8 && atoi(e) <= 64) ? atoi(e) : 32;
+    }
+    const int wpc = (p.epi == EPI_LOGITS) ? 8 : static_wpc;
+    if (p.epi != EPI_LOGITS) cap = std::max(cap, 4096);
+    if (tiles <= (int64_t)wpc * n_cu) {
         // waves per workgroup: small matrices spread over more CUs in
         // workgroups of 2 waves (measured faster up to ~1024 tiles), larger
         // ones in workgroups of 4 (MAK_GEMV_STATIC_WAVES overrides: 1, 2, 4)
