@@ -608,7 +608,7 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
         int w = sw ? sw : (waves1 <= 1024 ? 2 : 4);
         if (ks_env && 2 * tiles <= (int64_t)ks_wpc * n_cu && w >= 2 && gemv1_fn_ks(p, 2)) p.ks = 2;
         const int64_t waves = tiles * p.ks;
-        if (!sw) w = waves <= 1024 ? 2 : 4;
+        if (!sw) w = waves <= 2048 ? 2 : 4;   // (split waves: 2048 measured faster than 1024 for the 135M down GEMV's 1152)
         // RMSNorm staging holds 2 chunks of 8 inputs per thread
         while (p.in_kind != IN_RAW && w < 4 && 64 * w * 16 < p.geo.k) w *= 2;
         p.threads = 64 * w;
