@@ -328,6 +328,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the 1B-shape measurement")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the batched-decode and long-context measurements")
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, SECONDARY],
+                    help="batch-1 workload of the main line (the other one goes to `secondary`)")
     ap.add_argument("--max-new", type=int, default=0,
                     help="override the greedy token count (short counter-collection runs only)")
     args = ap.parse_args()
@@ -340,7 +342,9 @@ def main():
     if not os.path.exists(mak.LIB_PATH):
         from transformer_forward_pass_amd import build as B
         B.build()
-    r = measure(args, WORKLOAD, args.steps)
+    primary = args.workload
+    other = SECONDARY if primary == WORKLOAD else WORKLOAD
+    r = measure(args, primary, args.steps)
     wl = r["wl"]
     p0, n = len(r["prompt"]), wl.max_new
     r["roofline"]["traffic"] = measured_traffic(r["roofline"]["kernel"])
@@ -358,7 +362,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of 8) + "
-                               "%d greedy tokens, batch 1" % (WORKLOAD, p0, n),
+                               "%d greedy tokens, batch 1" % (primary, p0, n),
                    "accumulate": "f64"},
         "roofline": r["roofline"],
         "token_roofline": r["token_roofline"],
@@ -366,9 +370,9 @@ def main():
         "runs_ms": r["runs_ms"],
     }
     if not args.no_secondary:
-        r2 = measure(args, SECONDARY, max(2, args.steps // 2))
+        r2 = measure(args, other, max(2, args.steps // 2))
         out["secondary"] = {"workload": "%s-shaped random-init decoder: 32-token prompt + 128 greedy "
-                                        "tokens, batch 1" % SECONDARY,
+                                        "tokens, batch 1" % other,
                             "value": round(r2["tok_s"], 2), "unit": "tok/s",
                             "ms_per_step": round(r2["ms_per_step"], 4),
                             "roofline": r2["roofline"], "token_roofline": r2["token_roofline"],

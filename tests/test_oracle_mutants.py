@@ -3,18 +3,18 @@
 Each case plants one mistake (a dropped term, a wrong sign or index, a
 swapped operand, a wrong tie rule) in a temporary copy of the oracle, on the
 CPU, and runs the pin tests of test_oracle_ops / test_oracle_model /
-test_oracle_formats against it.  At least one pin must fail for every
+test_oracle_formats / test_oracle_rounding against it.  At least one pin must fail for every
 mutant, and all must pass for the unmodified copy."""
 import importlib.util
 import inspect
 import os
-import shutil
 
 import pytest
 
 from tests import test_oracle_formats as F
 from tests import test_oracle_model as M
 from tests import test_oracle_ops as P
+from tests import test_oracle_rounding as R
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -35,6 +35,18 @@ C_MUTANTS = {
     "residual-dropped": ("x[i] = rbf(x[i] + y[i], rnd);", "x[i] = rbf(y[i], rnd);"),
     "argmax-last-tie": ("if (v[i] > v[best]) best = i;", "if (v[i] >= v[best]) best = i;"),
     "bf16-round-half-up": ("u += 0x7fffu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    # the bf16 rounding points of the eager-bf16 reading
+    "attn-score-single-rounding": ("scores[j] = rbf(rbf(acc, rnd) * sc, rnd);", "scores[j] = rbf(acc * sc, rnd);"),
+    "attn-probs-fp32": ("scores[j] = rbf(r32(scores[j] / z, rnd), rnd);", "scores[j] = r32(scores[j] / z, rnd);"),
+    "attn-output-fp32": ("o[i] = rbf(acc, rnd);", "o[i] = r32(acc, rnd);"),
+    "rope-products-unrounded": ("u[i] = rbf(rbf(a * c[i], rnd) - rbf(b * s[i], rnd), rnd);\n"
+                                "        u[i + h] = rbf(rbf(b * c[i], rnd) + rbf(a * s[i], rnd), rnd);",
+                                "u[i] = rbf(a * c[i] - b * s[i], rnd);\n"
+                                "        u[i + h] = rbf(b * c[i] + a * s[i], rnd);"),
+    "swiglu-silu-unrounded": ("double z = rbf(g[i] / (1.0 + exp(-g[i])), rnd);",
+                              "double z = r32(g[i] / (1.0 + exp(-g[i])), rnd);"),
+    "rmsnorm-single-rounding": ("double xh = rbf(r32(x[k] * r, rnd), rnd);", "double xh = r32(x[k] * r, rnd);"),
+    "residual-fp32": ("x[i] = rbf(x[i] + y[i], rnd);", "x[i] = r32(x[i] + y[i], rnd);"),
 }
 
 PY_MUTANTS = {
@@ -44,12 +56,22 @@ PY_MUTANTS = {
                                "Kx[t, g] = rope(Kx[t, g], pos + 1, s.rope_theta, rnd)"),
     "final-norm-skipped": ("hf = rmsnorm(x, self.w[\"final_norm\"], self.s.rms_eps, self.rnd)",
                            "hf = x"),
+    "logits-rounded-bf16": ("return linear(self.lm, hf, OUT_F32, self.rnd)",
+                            "return linear(self.lm, hf, OUT_BF16, self.rnd)"),
+    "q-projection-fp32": ("Q = linear(lw[\"wq\"], Hn, OUT_BF16, rnd)", "Q = linear(lw[\"wq\"], Hn, OUT_F32, rnd)"),
+    "down-projection-fp32": ("D = linear(lw[\"w_down\"], M, OUT_BF16, rnd)", "D = linear(lw[\"w_down\"], M, OUT_F32, rnd)"),
+    "qk-norm-after-rope": ("                if s.qk_norm:\n"
+                           "                    Q[t, h] = rmsnorm(Q[t, h], lw[\"q_norm\"], s.rms_eps, rnd)\n"
+                           "                Q[t, h] = rope(Q[t, h], pos, s.rope_theta, rnd)",
+                           "                Q[t, h] = rope(Q[t, h], pos, s.rope_theta, rnd)\n"
+                           "                if s.qk_norm:\n"
+                           "                    Q[t, h] = rmsnorm(Q[t, h], lw[\"q_norm\"], s.rms_eps, rnd)"),
 }
 
 
 def _pins():
     pins = []
-    for mod in (F, P, M):
+    for mod in (F, P, M, R):
         for name, fn in sorted(vars(mod).items()):
             if not name.startswith("test_") or not callable(fn):
                 continue
