@@ -311,9 +311,12 @@ using namespace mak;
 
 #define MAK_SPLIT_DIMS(X) X(16) X(32) X(64) X(128)
 
+int mak_check_launch(const void* fn, dim3 grid, dim3 block, size_t lds);
+
 static hipError_t launch3(const void* fn, dim3 grid, dim3 block, const AttnPhase& p, hipStream_t st, hipEvent_t e0,
                           hipEvent_t e1)
 {
+    if (mak_check_launch(fn, grid, block, 0)) return hipErrorInvalidConfiguration;
     AttnPhase q = p;
     void* args[] = {&q};
     if (e0 || e1) return hipExtLaunchKernel(fn, grid, block, args, 0, st, e0, e1, 0);

@@ -626,10 +626,61 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
 
 // Launch `fn`; with start/stop events, HIP stamps them at the kernel's own
 // begin and end (the dispatch packet's timestamps), not around the launch.
+// Launch-configuration check of `fn` (mak_launch_check with the kernel's own
+// attributes, cached per kernel, and the device's LDS per workgroup).
+// Returns 0 or the violated rule; `msg` receives a description.
+static thread_local char g_launch_msg[256];
+
+const char* mak_launch_check_msg() { return g_launch_msg; }
+
+int mak_check_launch(const void* fn, dim3 grid, dim3 block, size_t lds)
+{
+    struct AttrEntry {
+        const void* fn;
+        int64_t max_threads, static_lds, max_dyn;
+    };
+    static AttrEntry cache[512];
+    static int n_cache = 0;
+    static int64_t lds_per_block = 0;
+    if (!lds_per_block) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+            lds_per_block = v;
+        else
+            lds_per_block = 160 * 1024;
+    }
+    const AttrEntry* e = nullptr;
+    for (int i = 0; i < n_cache; i++)
+        if (cache[i].fn == fn) e = &cache[i];
+    AttrEntry fresh{};
+    if (!e) {
+        hipFuncAttributes a{};
+        if (hipFuncGetAttributes(&a, fn) != hipSuccess) {
+            snprintf(g_launch_msg, sizeof g_launch_msg, "hipFuncGetAttributes failed for a kernel");
+            return 5;
+        }
+        fresh = {fn, a.maxThreadsPerBlock, (int64_t)a.sharedSizeBytes,
+                 a.maxDynamicSharedSizeBytes > 0 ? (int64_t)a.maxDynamicSharedSizeBytes : lds_per_block};
+        if (n_cache < 512) cache[n_cache++] = fresh;
+        e = &fresh;
+    }
+    const int rc = mak_launch_check(grid.x, grid.y, grid.z, block.x, block.y, block.z, e->max_threads, e->static_lds,
+                                    (int64_t)lds, e->max_dyn, lds_per_block);
+    if (rc)
+        snprintf(g_launch_msg, sizeof g_launch_msg,
+                 "launch rejected (rule %d): grid %ux%ux%u, block %ux%ux%u of at most %lld threads, "
+                 "LDS %zu dynamic (ceiling %lld) + %lld static of %lld",
+                 rc, grid.x, grid.y, grid.z, block.x, block.y, block.z, (long long)e->max_threads, lds,
+                 (long long)e->max_dyn, (long long)e->static_lds, (long long)lds_per_block);
+    return rc;
+}
+
 static hipError_t launch_fn(const void* fn, dim3 grid, dim3 block, void** args, size_t lds, hipStream_t st,
                             hipEvent_t e0, hipEvent_t e1)
 {
     if (!fn) return hipErrorInvalidValue;
+    if (mak_check_launch(fn, grid, block, lds)) return hipErrorInvalidConfiguration;
     if (e0 || e1) return hipExtLaunchKernel(fn, grid, block, args, lds, st, e0, e1, 0);
     return hipLaunchKernel(fn, grid, block, args, lds, st);
 }

@@ -33,6 +33,8 @@ size_t mak_attn_lds(const AttnPhase& p);
 int mak_gemv_nc(int ncols);
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n);
 size_t mak_gemv_lds(const GemvPhase& p);
+int mak_check_launch(const void* fn, dim3 grid, dim3 block, size_t lds);
+const char* mak_launch_check_msg();
 
 namespace {
 
@@ -259,6 +261,17 @@ uint16_t host_bf16(float f)
 
 }  // namespace
 
+// Scratch of one step: the LM head's per-workgroup argmax partials
+// ([kMaxGemvBlocks][MAK_MAX_COLS] value and index) and the split-KV
+// attention's scores, chunk maxima and partial outputs.
+struct StepScratch {
+    float* part_val;
+    int32_t* part_idx;
+    float* att_sc;
+    float* att_cmax;
+    double* att_opart;
+};
+
 struct PhaseTiming {
     bool on = false;
     struct Pending {
@@ -315,13 +328,16 @@ template <class F>
 int launch(mak_model* m, int kind, F&& fn)
 {
     hipEvent_t a = nullptr, b = nullptr;
-    if (m->tm.on) {
+    const bool timed = m->tm.on;
+    if (timed) {
         a = take_event(m);
         b = take_event(m);
         if (!a || !b) return fail(MAK_EDEVICE, "hipEventCreate failed");
     }
-    HIP_TRY(fn(a, b));
-    if (m->tm.on) m->tm.pending.push_back({a, b, kind});
+    const hipError_t e = fn(a, b);
+    if (e == hipErrorInvalidConfiguration) return fail(MAK_EINVAL, "%s", mak_launch_check_msg());
+    if (e != hipSuccess) return fail(MAK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    if (timed) m->tm.pending.push_back({a, b, kind});
     return MAK_OK;
 }
 
@@ -378,8 +394,9 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
 
 // Launch one step of the program on m->cur for the columns currently in the
 // control block: ncols columns; LM head (with argmax feedback) for
-// [lm_begin, lm_begin + lm_count).
-int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, bool split)
+// [lm_begin, lm_begin + lm_count).  `sc` holds the step's scratch buffers.
+int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, bool split,
+                const StepScratch& sc)
 {
     const mak_config& c = m->cfg;
     const Layout& L = m->L;
@@ -431,9 +448,9 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
         a.max_seq = c.max_seq;
         a.eps = c.rms_eps;
         a.scale = (float)(1.0 / std::sqrt((double)d));
-        a.sc = m->at<float>(L.att_sc);
-        a.cmax = m->at<float>(L.att_cmax);
-        a.opart = m->at<double>(L.att_opart);
+        a.sc = sc.att_sc;
+        a.cmax = sc.att_cmax;
+        a.opart = sc.att_opart;
         a.n_chunks = L.n_chunks;
         a.s_cap = L.s_cap;
         if (mak_attn_lds(a) > (size_t)kAttnLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
@@ -506,12 +523,32 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
         p.x_ld = H;
         p.logits = m->at<float>(L.logits);
         p.logits_ld = c.vocab;
-        p.part_val = m->at<float>(L.part_val);
-        p.part_idx = m->at<int32_t>(L.part_idx);
+        p.part_val = sc.part_val;
+        p.part_idx = sc.part_idx;
         p.out_tokens = d_out_tokens;
         p.ctl = ctl;
         int rc = run_gemv(m, MAK_PHASE_LMHEAD, p, lm_count, lm_begin);
         if (rc) return rc;
+    }
+    return MAK_OK;
+}
+
+// Every kernel node of a captured step graph must satisfy the launch rules
+// its launch was checked against (grid, workgroup bound, LDS ceilings).
+int check_graph(hipGraph_t graph)
+{
+    size_t n = 0;
+    HIP_TRY(hipGraphGetNodes(graph, nullptr, &n));
+    std::vector<hipGraphNode_t> nodes(n);
+    if (n) HIP_TRY(hipGraphGetNodes(graph, nodes.data(), &n));
+    for (size_t i = 0; i < n; i++) {
+        hipGraphNodeType t;
+        HIP_TRY(hipGraphNodeGetType(nodes[i], &t));
+        if (t != hipGraphNodeTypeKernel) continue;
+        hipKernelNodeParams kp{};
+        HIP_TRY(hipGraphKernelNodeGetParams(nodes[i], &kp));
+        if (mak_check_launch(kp.func, kp.gridDim, kp.blockDim, kp.sharedMemBytes))
+            return fail(MAK_EINVAL, "captured node %zu: %s", i, mak_launch_check_msg());
     }
     return MAK_OK;
 }
@@ -522,12 +559,20 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
 // slots) from the control block, so one graph serves every step of a shape.
 // max_n = the largest pos + 1 among the step's columns: above the model's
 // threshold (or past the single-pass capacity) attention runs split-KV.
+StepScratch arena_scratch(const mak_model* m)
+{
+    const Layout& L = m->L;
+    return StepScratch{m->at<float>(L.part_val), m->at<int32_t>(L.part_idx), m->at<float>(L.att_sc),
+                       m->at<float>(L.att_cmax), m->at<double>(L.att_opart)};
+}
+
 int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, int max_n)
 {
     const bool split = max_n > m->split_above || max_n > m->L.s_cap;
+    const StepScratch sc = arena_scratch(m);
     if (!m->use_graphs || m->tm.on) {
         m->cur = m->stream;
-        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split);
+        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split, sc);
     }
     for (const StepGraph& g : m->graphs)
         if (g.ncols == ncols && g.lm_begin == lm_begin && g.lm_count == lm_count && g.split == (int)split) {
@@ -537,7 +582,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
     hipGraph_t graph = nullptr;
     HIP_TRY(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal));
     m->cur = m->capture;
-    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split);
+    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split, sc);
     hipError_t e = hipStreamEndCapture(m->capture, &graph);
     m->cur = m->stream;
     if (rc) {
@@ -545,6 +590,10 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         return rc;
     }
     if (e != hipSuccess) return fail(MAK_EDEVICE, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    if ((rc = check_graph(graph))) {
+        (void)hipGraphDestroy(graph);
+        return rc;
+    }
     StepGraph sg{ncols, lm_begin, lm_count, (int)split, nullptr};
     e = hipGraphInstantiate(&sg.exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);

@@ -122,3 +122,25 @@ struct AttnPhase {
     int32_t n_chunks;         // ceil(max_seq / MAK_ATTN_CHUNK)
     int32_t s_cap;            // single-pass kernel: most positions its LDS score row holds
 };
+
+// ---------------------------------------------------------------------------
+// Launch-configuration check, applied to every launch before it is issued
+// and to every kernel node of a captured step graph: a grid of at least one
+// workgroup in each dimension, a workgroup no larger than the kernel's
+// compiled bound (its __launch_bounds__), dynamic LDS within the kernel's
+// dynamic-LDS ceiling, and static plus dynamic LDS within the device's LDS
+// per workgroup (160 KiB on gfx950).  Returns 0 when the launch is valid,
+// else the number of the first violated rule (1 grid, 2 workgroup size,
+// 3 dynamic-LDS ceiling, 4 total LDS).
+// ---------------------------------------------------------------------------
+static inline int mak_launch_check(uint32_t gx, uint32_t gy, uint32_t gz, uint32_t bx, uint32_t by, uint32_t bz,
+                                   int64_t max_threads, int64_t static_lds, int64_t dyn_lds,
+                                   int64_t max_dyn_lds, int64_t lds_per_block)
+{
+    if (gx < 1 || gy < 1 || gz < 1) return 1;
+    const int64_t threads = (int64_t)bx * by * bz;
+    if (threads < 1 || threads > max_threads) return 2;
+    if (dyn_lds < 0 || dyn_lds > max_dyn_lds) return 3;
+    if (static_lds + dyn_lds > lds_per_block) return 4;
+    return 0;
+}
