@@ -116,6 +116,26 @@ int mak_prefill(mak_model *m, int32_t slot, const int32_t *ids, int32_t n, int32
 int mak_decode_step(mak_model *m, int32_t slot, int32_t token, int32_t pos, float *d_logits,
                     int32_t *next_token);
 
+/* mak_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The call allocates nothing (no hipMalloc/hipFree, no graph
+ * instantiation, no events): it launches the step's phases one by one on the
+ * model's stream and takes the step's scratch (the LM head's argmax partials
+ * and the split-KV attention's scores, chunk maxima and partial outputs)
+ * from a static device array of 4 MiB that each GPU holds until the process
+ * ends, instead of the arena.  d_logits (device, [vocab] fp32, may be NULL)
+ * and d_next_token (device, one int32, may be NULL) receive the results by
+ * device-to-device copies.  The call returns once the work is queued; it
+ * does not synchronise the stream.  Results are bitwise those of
+ * mak_decode_step.  Returns MAK_EINVAL if the model's shape needs more step
+ * scratch than the static array holds (n_q_heads * max_seq * 4 +
+ * n_q_heads * ceil(max_seq/128) * (head_dim * 8 + 4) + 128 KiB, 256-byte
+ * aligned parts).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (two models, or two streams) race and must be
+ * serialised by the caller. */
+int mak_decode_step_static(mak_model *m, int32_t slot, int32_t token, int32_t pos, float *d_logits,
+                           int32_t *d_next_token);
+
 /* Greedy generation ("model-as-a-kernel", Usage: generate): reset `slot`,
  * prefill the n-token prompt from position 0, then emit exactly max_new tokens
  * into out_tokens (host, [max_new]); the first is the argmax of the prefill

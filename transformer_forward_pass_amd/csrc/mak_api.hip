@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -35,6 +36,18 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n);
 size_t mak_gemv_lds(const GemvPhase& p);
 int mak_check_launch(const void* fn, dim3 grid, dim3 block, size_t lds);
 const char* mak_launch_check_msg();
+
+// ---------------------------------------------------------------------------
+// Static scratch of mak_decode_step_static: the step's scratch buffers
+// (argmax partials, split-KV scores, chunk maxima and partial outputs of one
+// column) in a fixed device array instead of the arena, for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses the array's name as an address:
+// the device address is looked up once per device (hipGetSymbolAddress,
+// with that device current) and kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -304,6 +317,8 @@ struct mak_model {
     size_t arena_bytes;
     hipStream_t stream;
     std::vector<int32_t> slot_len;   // cached positions per slot
+    int device = 0;                  // the GPU current at mak_load
+    bool untimed = false;            // launches carry no timing events (the static-scratch step)
     template <class T>
     T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
 };
@@ -328,7 +343,7 @@ template <class F>
 int launch(mak_model* m, int kind, F&& fn)
 {
     hipEvent_t a = nullptr, b = nullptr;
-    const bool timed = m->tm.on;
+    const bool timed = m->tm.on && !m->untimed;
     if (timed) {
         a = take_event(m);
         b = take_event(m);
@@ -642,6 +657,59 @@ int check_model(const mak_model* m)
     return MAK_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the
+// first call for that device).
+int static_scratch_ptr(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return fail(MAK_EDEVICE, "device %d beyond the static scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MAK_EDEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MAK_OK;
+}
+
+// Carve one column's step scratch out of the static array; MAK_EINVAL if
+// this model's shape needs more than the array holds.
+int static_step_scratch(const mak_model* m, StepScratch* out)
+{
+    void* base = nullptr;
+    int rc = static_scratch_ptr(m->device, &base);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    const size_t part = (size_t)kMaxGemvBlocks * MAK_MAX_COLS * 4;
+    const size_t sc = (size_t)c.n_q_heads * c.max_seq * 4;
+    const size_t cm = (size_t)c.n_q_heads * m->L.n_chunks * 4;
+    const size_t op = (size_t)c.n_q_heads * m->L.n_chunks * c.head_dim * 8;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    const size_t o_pv = take(part), o_pi = take(part), o_sc = take(sc), o_cm = take(cm), o_op = take(op);
+    if (off > kStaticScratchBytes)
+        return fail(MAK_EINVAL,
+                    "this model needs %zu bytes of step scratch (n_q_heads %d, max_seq %d, head_dim %d); "
+                    "the static scratch holds %zu",
+                    off, c.n_q_heads, c.max_seq, c.head_dim, kStaticScratchBytes);
+    char* b = static_cast<char*>(base);
+    *out = StepScratch{reinterpret_cast<float*>(b + o_pv), reinterpret_cast<int32_t*>(b + o_pi),
+                       reinterpret_cast<float*>(b + o_sc), reinterpret_cast<float*>(b + o_cm),
+                       reinterpret_cast<double*>(b + o_op)};
+    return MAK_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -741,8 +809,15 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
     }
     HIP_TRY(hipStreamSynchronize(st));
 
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    {
+        void* unused = nullptr;   // once per device, with that device current
+        if ((rc = static_scratch_ptr(dev, &unused))) return rc;
+    }
     mak_model* m = new (std::nothrow) mak_model();
     if (!m) return fail(MAK_ENOMEM, "host allocation failed");
+    m->device = dev;
     m->cfg = c;
     m->L = std::move(L);
     m->arena = A;
@@ -910,6 +985,46 @@ int mak_decode_step(mak_model* m, int32_t slot, int32_t token, int32_t pos, floa
                                m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
     if ((rc = collect_timing(m))) return rc;
+    m->slot_len[slot] = pos + 1;
+    return MAK_OK;
+}
+
+int mak_decode_step_static(mak_model* m, int32_t slot, int32_t token, int32_t pos, float* d_logits,
+                           int32_t* d_next_token)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    const mak_config& c = m->cfg;
+    if (slot < 0 || slot >= c.max_batch) return fail(MAK_ERANGE, "slot %d out of range", slot);
+    if (token < 0 || token >= c.vocab) return fail(MAK_ERANGE, "token %d out of range", token);
+    if (pos < 0 || pos >= c.max_seq) return fail(MAK_ERANGE, "pos %d out of range", pos);
+    if (pos > m->slot_len[slot])
+        return fail(MAK_ERANGE, "pos %d beyond cached length %d", pos, m->slot_len[slot]);
+    StepScratch sc{};
+    if ((rc = static_step_scratch(m, &sc))) return rc;
+    ColState cs{};
+    cs.token = token;
+    cs.pos = pos;
+    cs.slot = slot;
+    cs.first_pos = pos;
+    cs.first_col = 0;
+    // one launch per phase on the model's stream: no graph, no events
+    m->untimed = true;
+    rc = set_cols(m, &cs, 1, 0);
+    if (!rc) {
+        const int max_n = pos + 1;
+        const bool split = max_n > m->split_above || max_n > m->L.s_cap;
+        m->cur = m->stream;
+        rc = record_step(m, 1, 0, 1, m->at<int32_t>(m->L.out_tokens), split, sc);
+    }
+    m->untimed = false;
+    if (rc) return rc;
+    if (d_logits)
+        HIP_TRY(hipMemcpyAsync(d_logits, m->at<float>(m->L.logits), (size_t)c.vocab * 4, hipMemcpyDeviceToDevice,
+                               m->stream));
+    if (d_next_token)
+        HIP_TRY(hipMemcpyAsync(d_next_token, m->at<int32_t>(m->L.out_tokens), 4, hipMemcpyDeviceToDevice,
+                               m->stream));
     m->slot_len[slot] = pos + 1;
     return MAK_OK;
 }

@@ -20,7 +20,7 @@ MAK_OK, MAK_EINVAL, MAK_ERANGE, MAK_ENOMEM, MAK_EDEVICE = 0, -1, -2, -3, -4
 MAK_MAX_BATCH = 16
 MAK_PREFILL_CHUNK = 8
 
-EXPORTS = ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_generate",
+EXPORTS = ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_decode_step_static", "mak_generate",
            "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",
            "mak_set_attention_split", "mak_set_prefill_chunk", "mak_set_phase_timing",
            "mak_phase_times", "mak_free", "mak_last_error")
@@ -76,6 +76,7 @@ def lib():
                                ctypes.c_size_t, P, ctypes.POINTER(P)]
         L.mak_prefill.argtypes = [P, I32, P, I32, I32, P]
         L.mak_decode_step.argtypes = [P, I32, I32, I32, P, P]
+        L.mak_decode_step_static.argtypes = [P, I32, I32, I32, P, P]
         L.mak_generate.argtypes = [P, I32, P, I32, I32, P]
         L.mak_decode_batch.argtypes = [P, I32, P, P, P, I32, P, P]
         L.mak_batch_max.argtypes = [P]
@@ -89,7 +90,7 @@ def lib():
         L.mak_free.argtypes = [P]
         L.mak_free.restype = None
         L.mak_last_error.restype = ctypes.c_char_p
-        for n in ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_generate",
+        for n in ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_decode_step_static", "mak_generate",
                   "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",
                   "mak_set_phase_timing", "mak_phase_times"):
             getattr(L, n).restype = ctypes.c_int
@@ -170,6 +171,15 @@ class MakModel:
                                      ctypes.c_void_p(lg.data_ptr()) if lg is not None else None,
                                      ctypes.byref(nxt)))
         return (lg[0] if lg is not None else None), nxt.value
+
+    def decode_step_static(self, token: int, pos: int, d_logits, d_next, slot: int = 0):
+        """mak_decode_step_static: results into caller-allocated device
+        tensors (fp32 [V] logits and one int32, either may be None); the
+        call only queues the work on the model's stream."""
+        _check(lib().mak_decode_step_static(
+            self.h, slot, int(token), int(pos),
+            ctypes.c_void_p(d_logits.data_ptr()) if d_logits is not None else None,
+            ctypes.c_void_p(d_next.data_ptr()) if d_next is not None else None))
 
     def prefill(self, ids: Sequence[int], start_pos: int = 0, slot: int = 0,
                 want_logits: bool = True):
