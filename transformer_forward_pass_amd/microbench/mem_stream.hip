@@ -7,6 +7,7 @@
 // 3. one-shot reads the size of a small decode phase (the whole read issued
 //    at once by B blocks of 4 waves, Q loads per lane), timed from launch to
 //    completion.
+// 4. a few workgroups of 16 waves streaming alone (1, 3 or 8 CUs busy).
 // Every loop is bounded by its arguments; all indices stay inside the buffers
 // (checked on the host before each launch).
 //
@@ -78,6 +79,29 @@ __global__ __launch_bounds__(256) void k_oneshot(const uint4* __restrict__ buf, 
     if (acc.x == 0x12345678u && acc.w == 0x9abcdef0u) sink[threadIdx.x] = acc;
 }
 
+// a few workgroups of 16 waves streaming alone (what one CU can pull while
+// the rest of the chip is idle): `rounds` rounds of Q wave-contiguous 1 KiB
+// loads per wave
+template <int Q>
+__global__ __launch_bounds__(1024) void k_cu_stream(const uint4* __restrict__ buf, size_t base, int rounds, uint4* sink)
+{
+    const int nw = gridDim.x * 16;
+    const int wave = blockIdx.x * 16 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < rounds; r++) {
+        const uint4* w = buf + base + ((size_t)r * nw + wave) * Q * 64 + lane;
+        uint4 v[Q];
+#pragma unroll
+        for (int k = 0; k < Q; k++) v[k] = w[k * 64];
+#pragma unroll
+        for (int k = 0; k < Q; k++) {
+            acc.x ^= v[k].x;
+            acc.w ^= v[k].w;
+        }
+    }
+    if (acc.x == 0x12345678u && acc.w == 0x9abcdef0u) sink[threadIdx.x] = acc;
+}
+
 static float time_ms(hipEvent_t a, hipEvent_t b)
 {
     float ms;
@@ -107,6 +131,30 @@ static void oneshot(const uint4* buf, uint4* sink, int blocks, size_t n16, hipSt
     const double kb = blocks * 4.0 * Q * 1024 / 1024.0;
     std::printf("oneshot  blocks %4d  Q %2d  (%7.0f KiB): %6.2f us per kernel, %7.1f GB/s\n", blocks, Q, kb, us,
                 kb * 1024 / us / 1e3);
+}
+
+template <int Q>
+static void cu_stream(const uint4* buf, uint4* sink, int blocks, int rounds, size_t n16, hipStream_t st, hipEvent_t a,
+                      hipEvent_t b)
+{
+    const size_t region = (size_t)rounds * blocks * 16 * Q * 64;   // 16-byte units per launch
+    if (region > n16) return;
+    const int reps = 200;
+    const size_t n_reg = n16 / region;
+    const size_t hop = std::max<size_t>(1, n_reg / reps);
+    for (int i = 0; i < 10; i++)
+        hipLaunchKernelGGL(k_cu_stream<Q>, dim3(blocks), dim3(1024), 0, st, buf, (size_t)0, rounds, sink);
+    CK(hipEventRecord(a, st));
+    for (int i = 0; i < reps; i++) {
+        const size_t base = ((size_t)i * hop % n_reg) * region;   // base + region <= n16
+        hipLaunchKernelGGL(k_cu_stream<Q>, dim3(blocks), dim3(1024), 0, st, buf, base, rounds, sink);
+    }
+    CK(hipEventRecord(b, st));
+    CK(hipEventSynchronize(b));
+    const double us = 1e3 * time_ms(a, b) / reps;
+    const double kb = region * 16.0 / 1024.0;
+    std::printf("cu-stream blocks %2d of 16 waves  Q %2d  rounds %2d (%6.0f KiB): %6.2f us per kernel\n", blocks, Q,
+                rounds, kb, us);
 }
 
 template <int D>
@@ -180,6 +228,14 @@ int main()
         oneshot<3>(buf, sink, blocks, n16, st, a, b);
         oneshot<9>(buf, sink, blocks, n16, st, a, b);
         oneshot<16>(buf, sink, blocks, n16, st, a, b);
+    }
+    // 4. a few CUs streaming alone
+    for (int blocks : {1, 3, 8}) {
+        cu_stream<1>(buf, sink, blocks, 1, n16, st, a, b);
+        cu_stream<16>(buf, sink, blocks, 1, n16, st, a, b);
+        cu_stream<16>(buf, sink, blocks, 2, n16, st, a, b);
+        cu_stream<16>(buf, sink, blocks, 6, n16, st, a, b);
+        cu_stream<8>(buf, sink, blocks, 12, n16, st, a, b);
     }
     return 0;
 }
