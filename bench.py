@@ -27,6 +27,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -195,16 +197,57 @@ def measure(args, name, steps):
     }
 
 
-def cpu_baseline(shape, w, prompt, n_new):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_run(shape, w, prompt, n_new, threads):
+    """The oracle on one prompt: prefill time, then n_new - 1 decode steps."""
+    import ctypes
     from oracle import oracle as O
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(threads))
     o = O.Oracle(shape, w, max_len=len(prompt) + n_new + 1)
     t0 = time.perf_counter()
-    o.generate(prompt, n_new)
-    dt = time.perf_counter() - t0
-    return {"value": n_new / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": "the same model, %d-token prompt, %d greedy tokens (%.1f s)" % (
-                len(prompt), n_new, dt)}
+    lg = o.prefill(prompt)
+    t1 = time.perf_counter()
+    tok = int(np.argmax(lg))
+    for i in range(n_new - 1):
+        tok = int(np.argmax(o.decode_step(tok, len(prompt) + i)))
+    t2 = time.perf_counter()
+    return {"threads": int(threads), "prompt_tokens": len(prompt), "prefill_s": round(t1 - t0, 3),
+            "decode_steps": n_new - 1, "decode_s": round(t2 - t1, 3),
+            "decode_ms_per_token": round(1e3 * (t2 - t1) / max(1, n_new - 1), 2),
+            "generated_tok_s": round(n_new / (t2 - t0), 2)}
+
+
+def cpu_baseline(shape, w, prompt, n_new, w_1b=None):
+    """The CPU oracle (untuned) on bounded samples of the benchmark's
+    workloads, on this host: the 135M shape with all threads (the reported
+    value: generated tokens per second, prefill included) and with one
+    thread, and the 1B shape with all threads."""
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    main = _oracle_run(shape, w, prompt, n_new, threads)
+    one = _oracle_run(shape, w, prompt[:8], 4, 1)
+    detail = {"all_threads": main, "one_thread": one}
+    if w_1b is not None:
+        from transformer_forward_pass_amd import synth
+        wl = synth.WORKLOADS["llama-3.2-1b"]
+        detail["1b_all_threads"] = _oracle_run(wl.shape, w_1b, synth.make_prompts(wl)[0][:8], 4, threads)
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(threads)
+    return {"value": main["generated_tok_s"], "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "os_cpu_count": os.cpu_count(),
+            "sample": "the %s-shaped model: %d-token prompt then %d greedy tokens on %d threads (value); "
+                      "8-token prompt + 4 tokens on 1 thread; the 1B shape: 8-token prompt + 4 tokens on %d "
+                      "threads" % (shape.name, len(prompt), n_new, threads, threads),
+            "detail": detail}
 
 
 def measure_batched(args, name="tinyllama-1.1b", reps=2):
@@ -258,6 +301,12 @@ def measure_batched(args, name="tinyllama-1.1b", reps=2):
             "step_roofline": {"bytes_per_step": int(step_bytes),
                               "achieved_gbs": round(step_bytes / t_step / 1e9, 2),
                               "frac": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4)},
+            # fp64 rate of the dominant GEMM: 2 flops per weight per sequence
+            # (16-column groups run on the fp64 matrix cores, 8 on the VALU)
+            "mfma_roofline": {"bound": "mfma" if B >= 9 else "alu", "kernel": dom,
+                              "achieved": round(per_launch / 2 * 2 * B / avg_s / 1e12, 3),
+                              "peak": FP64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s (fp64)",
+                              "frac": round(per_launch * B / avg_s / 1e12 / FP64_MFMA_PEAK_TFLOPS, 4)},
             "phase_ms_per_step": {k: round(v[0] / 16, 4) for k, v in times.items()}}
 
 
@@ -316,6 +365,56 @@ def measure_long(args, name="qwen3-0.6b", reps=2):
             "prefill_weight_gbs": round(prefill_bytes / bestp / 1e9, 2),
             "prefill_ms_chunk16": round(bestp16 * 1e3, 3),
             "phase_ms_per_call": {k: round(v[0], 4) for k, v in times.items()}}
+
+
+FP64_MFMA_PEAK_TFLOPS = 78.6
+
+
+def measure_long_prefill(args, name="llama-3.2-1b-p2040", reps=2):
+    """Long-prompt prefill: a 2040-token prompt on the 1B shape in chunks of
+    16 (the GEMMs on the fp64 matrix cores; attention split-KV past 768
+    positions), and in chunks of 8 for comparison.  Reports the prompt's
+    prefill time and the fp64 rate of its weight GEMMs (2 flops per weight
+    per token) against the fp64 matrix peak."""
+    import torch
+    from transformer_forward_pass_amd import mak, synth
+    wl = synth.WORKLOADS[name]
+    shape = wl.shape
+    w = synth.make_weights(shape)
+    prompt = synth.make_prompts(wl)[0]
+    m = mak.MakModel(shape, w, device="cuda:0", max_seq=shape.max_seq)
+    res = {}
+    for chunk in (16, 8):
+        m.set_prefill_chunk(chunk)
+        m.prefill(prompt[:64], want_logits=False)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps if chunk == 16 else 1):
+            t0 = time.perf_counter()
+            m.prefill(prompt, want_logits=True)
+            torch.cuda.synchronize()
+            t = time.perf_counter() - t0
+            best = t if best is None else min(best, t)
+        res[chunk] = best
+    m.set_prefill_chunk(16)
+    m.set_phase_timing(True)
+    m.prefill(prompt, want_logits=True)
+    times = m.phase_times()
+    m.set_phase_timing(False)
+    m.free()
+    H, I, qd, kvd = shape.hidden, shape.intermediate, shape.q_dim, shape.kv_dim
+    layer_w = H * (qd + 2 * kvd) + qd * H + 3 * H * I
+    P = len(prompt)
+    gemm_flop = 2.0 * P * shape.n_layers * layer_w + 2.0 * shape.vocab * H
+    gemm_s = sum(times[k][0] for k in ("qkv", "o", "gateup", "down", "lmhead")) / 1e3
+    achieved = gemm_flop / gemm_s / 1e12
+    return {"workload": "%s-shaped random-init decoder: %d-token prompt, chunks of 16" % (shape.name, P),
+            "prefill_ms": round(res[16] * 1e3, 3), "prefill_tok_s": round(P / res[16], 1),
+            "prefill_ms_chunk8": round(res[8] * 1e3, 3),
+            "mfma_roofline": {"bound": "mfma", "kernel": "weight GEMMs (k_gemm16)", "achieved": round(achieved, 2),
+                              "peak": FP64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s (fp64)",
+                              "frac": round(achieved / FP64_MFMA_PEAK_TFLOPS, 4)},
+            "phase_ms": {k: round(v[0], 3) for k, v in times.items()}}
 
 
 def main():
@@ -384,8 +483,12 @@ def main():
         progress("16-sequence batched decode done")
         out["long_context"] = measure_long(args)
         progress("long-context run done")
+        out["long_prefill"] = measure_long_prefill(args)
+        progress("long-prompt prefill done")
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(r["shape"], r["w"], r["prompt"], args.cpu_new)
+        w_1b = r2["w"] if (not args.no_secondary and other == SECONDARY) else None
+        out["cpu_baseline"] = cpu_baseline(r["shape"], r["w"], r["prompt"], args.cpu_new, w_1b)
+        progress("CPU oracle baseline done")
     print(json.dumps(out))
 
 

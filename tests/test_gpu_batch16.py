@@ -2,8 +2,10 @@
 weights streamed once per step for all of them ("model-as-a-kernel", API:
 decode_batch).  Each sequence's tokens and logits must equal decoding it
 alone (the one-column kernels) bitwise, and match the CPU oracle.  Covers
-full (16) and padded (9, 13) column groups (each wave of the GEMVs stages
-two columns' RMSNorm rows), permuted slots, head_dim 64 and 32, GQA."""
+full (16) and padded (9, 13) column groups (each wave of the GEMMs stages
+two columns' RMSNorm rows), permuted slots, head_dim 64 and 32, GQA, a
+K = 4160 down projection and a 70001-row LM head (these steps run on the
+fp64 matrix cores)."""
 import dataclasses
 
 import numpy as np
@@ -18,6 +20,10 @@ SHAPES = {
     "tiny-d64": dataclasses.replace(synth.SHAPES["tiny"], max_batch=16),
     "d32-gqa3": synth.small_shape(n_layers=2, hidden=192, n_q_heads=6, n_kv_heads=2, head_dim=32,
                                   intermediate=344, vocab=1000, max_batch=16),
+    # a down projection wider than 4096 inputs and an LM head of more row
+    # groups than the argmax partials hold (its workgroups loop over them)
+    "wide": synth.small_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                              intermediate=4160, vocab=70001, max_batch=16),
 }
 STEPS = 3
 

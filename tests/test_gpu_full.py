@@ -10,9 +10,9 @@ vocabulary at three stored steps (max-abs <= 2e-2 and relative L2 <= 1e-3
 over [V]) and, at the other sampled steps, at 512 fixed vocabulary indices
 and the oracle's 16 largest logits.  Each benchmark configuration is covered
 at its own size: batch-1 decode of the 135M, 1B and Qwen3 shapes, Qwen3's
-512-token prompt in chunks of 16, and TinyLlama batches of 8 and 16
-sequences (16 columns run the down projection, K = 5632, as two launches of
-eight columns)."""
+512-token prompt in chunks of 16, TinyLlama batches of 8 and 16 sequences,
+and a 2040-token prompt on the 1B shape in chunks of 16 (long-prompt
+prefill; split-KV attention past 768 positions)."""
 import json
 import os
 
@@ -160,3 +160,19 @@ def test_full_workload_batched16_tinyllama():
     """16 sequences decoded together: the benchmark's 16-column step
     (checked over the first 32 of its 128 tokens)."""
     assert _batched("tinyllama-1.1b-b16") >= 8
+
+
+def test_long_prompt_prefill_1b():
+    """A 2040-token prompt on the 1B shape consumed 16 tokens per step (the
+    GEMMs on the fp64 matrix cores, attention split-KV past 768 positions):
+    the prompt's last-token logits and two teacher-forced decode steps over
+    [V], and the free-running stream."""
+    name = "llama-3.2-1b-p2040"
+    g, full, wl, m = _load(name)
+    seq = g["sequences"][0]
+    assert len(seq["prompt"]) == 2040
+    m.set_prefill_chunk(16)
+    got = m.generate(seq["prompt"], wl.max_new)
+    tokens_ok(got, seq["tokens"], seq["gaps"], name)
+    _teacher_forced(m, g, full, name, chunk=16)
+    m.free()

@@ -321,6 +321,10 @@ static const void* gemv_fn_r1(int epi)
     return nullptr;
 }
 
+// gemm16.hip: the multi-column GEMM on the fp64 matrix cores
+const void* mak_gemm16_fn(int rt, int epi, bool staged);
+size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round);
+
 // Column capacity (template NC) for n active columns.
 int mak_gemv_nc(int ncols) { return ncols <= 1 ? 1 : ncols <= 2 ? 2 : ncols <= 4 ? 4 : ncols <= 8 ? 8 : 16; }
 
@@ -353,6 +357,7 @@ static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn_ks(p, 1) != nul
 
 static const void* gemv_fn(const GemvPhase& p)
 {
+    if (p.multi == 2) return mak_gemm16_fn(p.rr, p.epi, p.in_kind != IN_RAW);
     if (p.multi) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
     if (const void* f = gemv1_fn(p)) return f;
     switch (p.geo.r) {
@@ -367,6 +372,10 @@ static int gemv_threads(const GemvPhase& p) { return p.threads; }
 
 size_t mak_gemv_lds(const GemvPhase& p)
 {
+    if (p.multi == 2) {
+        const int64_t groups = (p.geo.n_rows + 16 * p.rr - 1) / (16 * p.rr);
+        return mak_gemm16_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks);
+    }
     if (p.multi)
         return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.jw, p.geo.lr_log2, p.epi == EPI_SWIGLU);
     return (size_t)p.geo.k * sizeof(float);
@@ -533,6 +542,39 @@ static void gemvn_plan_auto(GemvPhase& p, size_t lds_budget, int cap)
 // tiles spread evenly so that every wave streams the same number of tiles.
 // Multi-column: the work split of gemvn_plan, one workgroup per group slot
 // up to the resident capacity.
+// Multi-column steps of at least this many columns run on the fp64 matrix
+// cores (k_gemm16); MAK_GEMM_MFMA_COLS overrides (0: never).  fp64 MFMA
+// sustains about 40 TFLOP/s here against 63 for fp64 VALU FMAs, so the
+// matrix cores pay only where they take the most multiply-adds off the
+// VALU: measured faster than k_gemvn for the 16-column groups (16-sequence
+// decode 3.17 -> 2.78 ms per step, 16-token prefill chunks), slower at 8.
+static int gemm16_min_cols()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("MAK_GEMM_MFMA_COLS");
+        v = (e && atoi(e) >= 0) ? atoi(e) : 9;
+    }
+    return v;
+}
+
+// Tiles of 16 rows per k_gemm16 workgroup: as many as still leave two
+// workgroups per CU, within the LDS budget.  Returns 0 if the kernel does
+// not apply (too few columns, or RMSNorm inputs wider than 4096).
+int mak_gemm16_plan(const GemvPhase& p, int ncols, size_t lds_budget)
+{
+    const int mc = gemm16_min_cols();
+    if (mc == 0 || ncols < mc || ncols > 16) return 0;
+    const bool staged = p.in_kind != IN_RAW;
+    if (staged && p.geo.k > 4096) return 0;
+    const int n_cu = device_cus();
+    const int n16 = (p.geo.n_rows + 15) / 16;
+    int rt = (n16 >= 8 * n_cu) ? 4 : (n16 >= 4 * n_cu) ? 2 : 1;
+    // (sized for the worst case: partial tiles beside the inputs)
+    while (rt > 1 && mak_gemm16_lds(rt, p.geo.k, staged, false) > lds_budget) rt >>= 1;
+    return mak_gemm16_lds(rt, p.geo.k, staged, false) <= lds_budget ? rt : 0;
+}
+
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
 {
     const int n_cu = device_cus();
@@ -540,6 +582,16 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
     // measured slower: its staging and combine cost more than the fold)
     p.multi = p.ncols >= 2;
     if (p.multi) {
+        if (const int rt = mak_gemm16_plan(p, p.ncols, lds_budget_n)) {
+            p.multi = 2;
+            p.rr = rt;
+            p.jw = 1;
+            p.threads = MAK_NBLOCK;
+            const int64_t groups = (p.geo.n_rows + 16 * rt - 1) / (16 * rt);
+            // (the LM head's argmax partials hold `cap` workgroups: its
+            // workgroups loop over the groups)
+            return (int)std::max<int64_t>(1, p.epi == EPI_LOGITS ? std::min<int64_t>(groups, cap) : groups);
+        }
         gemvn_plan(p, lds_budget_n, cap);
         p.threads = MAK_NBLOCK;
         const void* fn = gemv_fn(p);
@@ -749,6 +801,12 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
                 if (e != hipSuccess) return e;
             }
         }
+    for (int rt : {1, 2, 4})
+        for (int epi : {(int)EPI_STORE, (int)EPI_RESIDUAL, (int)EPI_SWIGLU, (int)EPI_LOGITS})
+            for (bool staged : {true, false}) {
+                hipError_t e = set(mak_gemm16_fn(rt, epi, staged), bytes_n);
+                if (e != hipSuccess) return e;
+            }
     for (int r : {1, 2, 4})
         for (int j : {1, 2, 3, 4, 6, 9, 11, 16})
             for (int ks : {1, 2})

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -34,6 +35,7 @@ size_t mak_attn_lds(const AttnPhase& p);
 int mak_gemv_nc(int ncols);
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n);
 size_t mak_gemv_lds(const GemvPhase& p);
+int mak_gemm16_plan(const GemvPhase& p, int ncols, size_t lds_budget);
 int mak_check_launch(const void* fn, dim3 grid, dim3 block, size_t lds);
 const char* mak_launch_check_msg();
 
@@ -297,9 +299,13 @@ struct PhaseTiming {
     int64_t launches[MAK_PHASE_COUNT] = {};
 };
 
-// A captured step: (ncols, lm_begin, lm_count, split attention) -> executable graph.
+// Attention kernel of a step: the single pass over an LDS score row (up to
+// 4096 positions), or split-KV.
+enum AttnMode { ATTN_SINGLE = 1, ATTN_SPLIT = 2 };
+
+// A captured step: (ncols, lm_begin, lm_count, attention mode) -> executable graph.
 struct StepGraph {
-    int ncols, lm_begin, lm_count, split;
+    int ncols, lm_begin, lm_count, attn;
     hipGraphExec_t exec;
 };
 
@@ -384,9 +390,12 @@ int max_cols_for_k(int k)
 
 int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
 {
-    // split the columns into groups whose inputs fit in LDS
-    const int step = (p.epi == EPI_LOGITS) ? ncols : max_cols_for_k(p.geo.k);
-    if (p.epi == EPI_LOGITS && max_cols_for_k(p.geo.k) < ncols)
+    // split the columns into groups whose inputs fit in LDS (the matrix-core
+    // kernel stages at most 16 RMSNorm inputs of K <= 4096 and reads raw
+    // inputs from memory: one launch)
+    const bool mfma = mak_gemm16_plan(p, ncols, kLdsBudgetN) != 0;
+    const int step = (p.epi == EPI_LOGITS || mfma) ? ncols : max_cols_for_k(p.geo.k);
+    if (p.epi == EPI_LOGITS && !mfma && max_cols_for_k(p.geo.k) < ncols)
         return fail(MAK_EINVAL, "LM head input too wide for %d columns", ncols);
     for (int c0 = 0; c0 < ncols; c0 += step) {
         GemvPhase q = p;
@@ -410,7 +419,7 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
 // Launch one step of the program on m->cur for the columns currently in the
 // control block: ncols columns; LM head (with argmax feedback) for
 // [lm_begin, lm_begin + lm_count).  `sc` holds the step's scratch buffers.
-int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, bool split,
+int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, int attn,
                 const StepScratch& sc)
 {
     const mak_config& c = m->cfg;
@@ -469,7 +478,7 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
         a.n_chunks = L.n_chunks;
         a.s_cap = L.s_cap;
         if (mak_attn_lds(a) > (size_t)kAttnLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
-        if (split) {
+        if (attn == ATTN_SPLIT) {
             for (int stage = 0; stage < 3; stage++)
                 if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
                          return mak_launch_attn_split(a, stage, m->cur, e0, e1);
@@ -581,23 +590,30 @@ StepScratch arena_scratch(const mak_model* m)
                        m->at<float>(L.att_cmax), m->at<double>(L.att_opart)};
 }
 
+// Attention kernel for a step whose longest context is max_n positions:
+// split-KV above the model's threshold or past the single-pass capacity.
+int attn_mode(const mak_model* m, int max_n)
+{
+    return (max_n > m->split_above || max_n > m->L.s_cap) ? ATTN_SPLIT : ATTN_SINGLE;
+}
+
 int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, int max_n)
 {
-    const bool split = max_n > m->split_above || max_n > m->L.s_cap;
+    const int attn = attn_mode(m, max_n);
     const StepScratch sc = arena_scratch(m);
     if (!m->use_graphs || m->tm.on) {
         m->cur = m->stream;
-        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split, sc);
+        return record_step(m, ncols, lm_begin, lm_count, d_out_tokens, attn, sc);
     }
     for (const StepGraph& g : m->graphs)
-        if (g.ncols == ncols && g.lm_begin == lm_begin && g.lm_count == lm_count && g.split == (int)split) {
+        if (g.ncols == ncols && g.lm_begin == lm_begin && g.lm_count == lm_count && g.attn == attn) {
             HIP_TRY(hipGraphLaunch(g.exec, m->stream));
             return MAK_OK;
         }
     hipGraph_t graph = nullptr;
     HIP_TRY(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal));
     m->cur = m->capture;
-    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens, split, sc);
+    int rc = record_step(m, ncols, lm_begin, lm_count, d_out_tokens, attn, sc);
     hipError_t e = hipStreamEndCapture(m->capture, &graph);
     m->cur = m->stream;
     if (rc) {
@@ -609,7 +625,7 @@ int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out
         (void)hipGraphDestroy(graph);
         return rc;
     }
-    StepGraph sg{ncols, lm_begin, lm_count, (int)split, nullptr};
+    StepGraph sg{ncols, lm_begin, lm_count, attn, nullptr};
     e = hipGraphInstantiate(&sg.exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return fail(MAK_EDEVICE, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
@@ -1012,10 +1028,8 @@ int mak_decode_step_static(mak_model* m, int32_t slot, int32_t token, int32_t po
     m->untimed = true;
     rc = set_cols(m, &cs, 1, 0);
     if (!rc) {
-        const int max_n = pos + 1;
-        const bool split = max_n > m->split_above || max_n > m->L.s_cap;
         m->cur = m->stream;
-        rc = record_step(m, 1, 0, 1, m->at<int32_t>(m->L.out_tokens), split, sc);
+        rc = record_step(m, 1, 0, 1, m->at<int32_t>(m->L.out_tokens), attn_mode(m, pos + 1), sc);
     }
     m->untimed = false;
     if (rc) return rc;

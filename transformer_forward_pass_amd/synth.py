@@ -114,6 +114,8 @@ WORKLOADS: Dict[str, Workload] = {
     # the same shape and weights, 16 sequences decoded together
     "tinyllama-1.1b-b16": Workload(dataclasses.replace(SHAPES["tinyllama-1.1b"], max_batch=16),
                                    prompt_len=16, max_new=128, batch=16, prompt_len_hi=256),
+    # long-prompt prefill: a 2040-token prompt on the 1B shape, in chunks of 16
+    "llama-3.2-1b-p2040": Workload(SHAPES["llama-3.2-1b"], prompt_len=2040, max_new=4, chunk=16),
 }
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
