@@ -196,12 +196,17 @@ class Oracle:
     ``shape`` provides n_layers, hidden, n_q_heads, n_kv_heads, head_dim,
     intermediate, vocab, rms_eps, rope_theta, tie_embeddings, qk_norm.
     ``weights`` is ``{"embed", "lm_head" or None, "final_norm", "layers"}``
-    of uint16 bf16 bit arrays in ``[out, in]`` layout.
+    of uint16 bf16 bit arrays in ``[out, in]`` layout.  A shape whose
+    ``weight_format`` is ``"mxfp4"`` runs on the dequantized 4-bit form of the
+    per-layer linear matrices (``mxfp4.py``), which are exactly bf16 values.
     """
 
     def __init__(self, shape, weights, *, rounding: bool = True, max_len: int = 2048,
                  n_seqs: int = 1):
         self.s = shape
+        if getattr(shape, "weight_format", "bf16") == "mxfp4":
+            from . import mxfp4
+            weights = mxfp4.dequantized_weights(shape, weights)
         self.w = weights
         self.rnd = bool(rounding)
         self.max_len = int(max_len)
