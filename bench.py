@@ -69,17 +69,22 @@ SECONDARY = "llama-3.2-1b"
 
 def _gemv_bytes(shape, kind):
     """Algorithmic bytes of one launch of a phase kind at batch 1: weight
-    bytes streamed once + activation vectors read and written (bf16)."""
+    bytes streamed once + activation vectors read and written (bf16).  A
+    4-bit (MXFP4) matrix of n weights streams n/2 code bytes and n/32 scale
+    bytes; the LM head stays bf16."""
     H, I, d = shape.hidden, shape.intermediate, shape.head_dim
     qd, kvd = shape.q_dim, shape.kv_dim
+
+    def wb(n):
+        return n // 2 + n // 32 if getattr(shape, "weight_format", "bf16") == "mxfp4" else 2 * n
     if kind == "qkv":
-        return 2 * (qd + 2 * kvd) * H + 2 * (H + H) + 2 * (qd + 2 * kvd)
+        return wb((qd + 2 * kvd) * H) + 2 * (H + H) + 2 * (qd + 2 * kvd)
     if kind == "o":
-        return 2 * H * qd + 2 * qd + 2 * 2 * H
+        return wb(H * qd) + 2 * qd + 2 * 2 * H
     if kind == "gateup":
-        return 2 * 2 * I * H + 2 * (H + H) + 2 * I
+        return wb(2 * I * H) + 2 * (H + H) + 2 * I
     if kind == "down":
-        return 2 * H * I + 2 * I + 2 * 2 * H
+        return wb(H * I) + 2 * I + 2 * 2 * H
     if kind == "lmhead":
         return 2 * shape.vocab * H + 2 * (H + H) + 4 * shape.vocab
     return None
@@ -485,6 +490,15 @@ def main():
         progress("long-context run done")
         out["long_prefill"] = measure_long_prefill(args)
         progress("long-prompt prefill done")
+        r4 = measure(args, "llama-3.2-1b-mxfp4", max(2, args.steps // 2))
+        out["mxfp4"] = {"workload": "llama-3.2-1b-shaped random-init decoder, per-layer linear weights in "
+                                    "4-bit OCP MXFP4 (LM head bf16): 32-token prompt + 128 greedy tokens, "
+                                    "batch 1",
+                        "value": round(r4["tok_s"], 2), "unit": "tok/s",
+                        "ms_per_step": round(r4["ms_per_step"], 4),
+                        "roofline": r4["roofline"], "token_roofline": r4["token_roofline"],
+                        "phase_ms_per_step": r4["phase_ms_per_step"], "runs_ms": r4["runs_ms"]}
+        progress("4-bit decode done")
     if not args.no_cpu:
         w_1b = r2["w"] if (not args.no_secondary and other == SECONDARY) else None
         out["cpu_baseline"] = cpu_baseline(r["shape"], r["w"], r["prompt"], args.cpu_new, w_1b)

@@ -49,9 +49,21 @@ extern "C" {
 #define MAK_MAX_BATCH 16    /* columns of one decode batch                          */
 #define MAK_PREFILL_CHUNK 8 /* prompts are consumed in chunks of at most 8 tokens    */
 
+/* Weight formats of the per-layer linear matrices (q, k, v, o, gate, up,
+ * down).  The embedding, the LM head and the norm weights stay bf16.
+ *   MAK_WEIGHTS_BF16   bf16, as given.
+ *   MAK_WEIGHTS_MXFP4  4-bit: mak_load quantizes each matrix with
+ *                      mak_quantize_mxfp4 and decoding streams the codes
+ *                      ("model-as-a-kernel", API section, "Supported"
+ *                      paragraph: 4-bit weights; the page's nf4 format is not
+ *                      specified there, so the 4-bit format is OCP MXFP4). */
+#define MAK_WEIGHTS_BF16 0
+#define MAK_WEIGHTS_MXFP4 1
+
 /* Model shape.  head_dim a power of two in [16, 128]; hidden, intermediate and
- * n_q_heads*head_dim multiples of 8; n_q_heads a multiple of n_kv_heads;
- * 1 <= max_batch <= MAK_MAX_BATCH; max_seq >= 1. */
+ * n_q_heads*head_dim multiples of 8 (of 32 with MAK_WEIGHTS_MXFP4);
+ * n_q_heads a multiple of n_kv_heads; 1 <= max_batch <= MAK_MAX_BATCH;
+ * max_seq >= 1. */
 typedef struct {
     int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
     float rms_eps, rope_theta;
@@ -59,6 +71,7 @@ typedef struct {
     int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before rope        */
     int32_t max_seq;        /* positions per KV slot                             */
     int32_t max_batch;      /* KV slots = sequences decodable at once            */
+    int32_t weight_format;  /* MAK_WEIGHTS_BF16 (0) or MAK_WEIGHTS_MXFP4         */
 } mak_config;
 
 /* One decoder layer's weights (host bf16 bits). q_norm/k_norm are [head_dim]
@@ -85,6 +98,20 @@ typedef struct {
 } mak_weights;
 
 typedef struct mak_model mak_model; /* opaque */
+
+/* 4-bit quantization (host only, no device work) of a [rows, k] bf16 matrix
+ * into OCP MXFP4 (Microscaling Formats specification v1.0), the format of
+ * MAK_WEIGHTS_MXFP4.  Each block of 32 consecutive weights of a row shares
+ * one scale 2^e with e = floor(log2(max |w| of the block)) - 2, clamped to
+ * [-127, 127] (-127 for an all-zero block), written to scales[row][k/32] as
+ * the E8M0 byte e + 127.  Each weight becomes the FP4 E2M1 code (sign, 2
+ * exponent bits, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) of
+ * w / 2^e rounded to nearest, ties to the even code, magnitudes above 6
+ * saturating to 6, zero with a clear sign bit; codes[row][k/2] holds two per
+ * byte, the lower-indexed weight in the low nibble.  Every dequantized value
+ * code * 2^e is exactly a bf16 value.  k must be a positive multiple of 32 and
+ * every weight finite (MAK_EINVAL otherwise, nothing written). */
+int mak_quantize_mxfp4(const uint16_t *w, int64_t rows, int32_t k, uint8_t *codes, uint8_t *scales);
 
 /* Device bytes mak_load needs for this shape: packed weights, rope tables,
  * max_batch KV slots of max_seq positions, and scratch.  No device work. */

@@ -103,5 +103,5 @@ if __name__ == "__main__":
     # tiny: the GPU tests compare it with the oracle run in-process; the
     # stored file is the record of the same run
     for n in (sys.argv[1:] or ["tiny", "smollm2-135m", "llama-3.2-1b", "qwen3-0.6b", "tinyllama-1.1b",
-                               "tinyllama-1.1b-b16", "llama-3.2-1b-p2040"]):
+                               "tinyllama-1.1b-b16", "llama-3.2-1b-p2040", "llama-3.2-1b-mxfp4"]):
         make(n)

@@ -56,6 +56,24 @@ def test_plan_rejects_bad_shapes(field, value):
     assert e.value.code == mak.MAK_EINVAL
 
 
+def test_plan_of_4bit_weights():
+    import dataclasses
+    s16 = synth.SHAPES["llama-3.2-1b"]
+    s4 = dataclasses.replace(s16, weight_format="mxfp4")
+    n16, n4 = mak.plan(s16), mak.plan(s4)
+    # the linear weights shrink from 2 bytes to 17/32 of a byte each
+    lin = s16.n_layers * (s16.hidden * (s16.q_dim + 2 * s16.kv_dim) + s16.q_dim * s16.hidden
+                          + 3 * s16.hidden * s16.intermediate)
+    saved = lin * 2 - (lin // 2 + lin // 32)
+    assert abs((n16 - n4) - saved) <= 64 * 2 ** 20
+    # 4-bit matrices need K a multiple of the 32-weight block
+    for field, value in (("intermediate", 688), ("hidden", 80)):
+        s = dataclasses.replace(synth.SHAPES["tiny"], weight_format="mxfp4", **{field: value})
+        with pytest.raises(mak.MakError) as e:
+            mak.plan(s)
+        assert e.value.code == mak.MAK_EINVAL
+
+
 def test_load_validates_before_touching_the_device():
     L = mak.lib()
     cfg = mak.make_config(synth.SHAPES["tiny"])

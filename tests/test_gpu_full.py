@@ -11,8 +11,10 @@ over [V]) and, at the other sampled steps, at 512 fixed vocabulary indices
 and the oracle's 16 largest logits.  Each benchmark configuration is covered
 at its own size: batch-1 decode of the 135M, 1B and Qwen3 shapes, Qwen3's
 512-token prompt in chunks of 16, TinyLlama batches of 8 and 16 sequences,
-and a 2040-token prompt on the 1B shape in chunks of 16 (long-prompt
-prefill; split-KV attention past 768 positions)."""
+a 2040-token prompt on the 1B shape in chunks of 16 (long-prompt
+prefill; split-KV attention past 768 positions), and the 1B shape with 4-bit
+(MXFP4) per-layer weights, against the oracle run on the dequantized
+weights."""
 import json
 import os
 
@@ -85,7 +87,7 @@ def _teacher_forced(m, g, full, name, chunk=None):
     return exact
 
 
-@pytest.mark.parametrize("name", ["smollm2-135m", "llama-3.2-1b", "qwen3-0.6b"])
+@pytest.mark.parametrize("name", ["smollm2-135m", "llama-3.2-1b", "qwen3-0.6b", "llama-3.2-1b-mxfp4"])
 def test_full_workload_single_sequence(name):
     g, full, wl, m = _load(name)
     seq = g["sequences"][0]

@@ -87,31 +87,44 @@ __device__ __forceinline__ void store_chunk_f32(float* dst, uint4 v)
 }
 
 // hs[c*K + k] as fp32 (bf16 values, exact): the fold then converts each
-// input element to fp64 with one instruction
-template <int NC>
+// input element to fp64 with one instruction.  PAD32 lays each column out in
+// blocks of 32 inputs at a stride of 36 floats (the 4-bit GEMV reads one
+// block per lane; the padding spreads neighbouring lanes' blocks over
+// distinct LDS banks): input k of column c at hs[c*CS + (k/32)*36 + k%32]
+// with CS = (K/32)*36.
+__host__ __device__ constexpr int pad32_stride(int k) { return (k >> 5) * 36; }
+
+template <bool PAD32>
+__device__ __forceinline__ int stage_off(int q)   // float offset of 8-input chunk q
+{
+    return PAD32 ? (q >> 2) * 36 + (q & 3) * 8 : 8 * q;
+}
+
+template <int NC, bool PAD32 = false>
 __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st, float* hs, double* red,
                                              const int NT)
 {
     constexpr int QPT = Staged<NC>::QPT;
     const int K = p.geo.k, C = K >> 3;
     const int tid = threadIdx.x;
+    const size_t cs = PAD32 ? (size_t)pad32_stride(K) : (size_t)K;
 #pragma unroll
     for (int c = 0; c < NC; c++) {
-        float* hc = hs + (size_t)c * K;
+        float* hc = hs + (size_t)c * cs;
         const int col = p.col0 + c;
         if (c >= p.ncols) {
-            for (int q = tid; q < C; q += NT) store_chunk_f32(hc + 8 * q, make_uint4(0, 0, 0, 0));
+            for (int q = tid; q < C; q += NT) store_chunk_f32(hc + stage_off<PAD32>(q), make_uint4(0, 0, 0, 0));
             continue;
         }
         if (p.in_kind == IN_RAW) {
 #pragma unroll
             for (int i = 0; i < QPT; i++) {
                 const int q = tid + i * NT;
-                if (q < C) store_chunk_f32(hc + 8 * q, st.v[c][i]);
+                if (q < C) store_chunk_f32(hc + stage_off<PAD32>(q), st.v[c][i]);
             }
             // chunks beyond what the registers held (K > QPT*2048)
             const uint4* src = reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
-            for (int q = tid + QPT * NT; q < C; q += NT) store_chunk_f32(hc + 8 * q, src[q]);
+            for (int q = tid + QPT * NT; q < C; q += NT) store_chunk_f32(hc + stage_off<PAD32>(q), src[q]);
             continue;
         }
         // RMSNorm of x: at most 2 chunks per thread (launches size the
@@ -147,7 +160,7 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
                     const uint32_t hi = rms_apply(bf_hi(u[e]), r, bf_hi(ww[e]));
                     o[e] = lo | (hi << 16);
                 }
-                store_chunk_f32(hc + 8 * q, make_uint4(o[0], o[1], o[2], o[3]));
+                store_chunk_f32(hc + stage_off<PAD32>(q), make_uint4(o[0], o[1], o[2], o[3]));
             }
         }
         lds_barrier();  // `red` is reused by the next column

@@ -325,6 +325,11 @@ static const void* gemv_fn_r1(int epi)
 const void* mak_gemm16_fn(int rt, int epi, bool staged);
 size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round);
 
+// gemv4.hip: the GEMV over 4-bit (MXFP4) weights
+const void* mak_gemv4_fn(int r, int nc, int epi);
+size_t mak_gemv4_lds(int k, int nc);
+hipError_t mak_gemv4_set_lds_limit(int bytes);
+
 // Column capacity (template NC) for n active columns.
 int mak_gemv_nc(int ncols) { return ncols <= 1 ? 1 : ncols <= 2 ? 2 : ncols <= 4 ? 4 : ncols <= 8 ? 8 : 16; }
 
@@ -357,6 +362,7 @@ static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn_ks(p, 1) != nul
 
 static const void* gemv_fn(const GemvPhase& p)
 {
+    if (p.geo.fmt == MAK_FMT_MXFP4) return mak_gemv4_fn(p.geo.r, mak_gemv_nc(p.ncols), p.epi);
     if (p.multi == 2) return mak_gemm16_fn(p.rr, p.epi, p.in_kind != IN_RAW);
     if (p.multi) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
     if (const void* f = gemv1_fn(p)) return f;
@@ -372,6 +378,7 @@ static int gemv_threads(const GemvPhase& p) { return p.threads; }
 
 size_t mak_gemv_lds(const GemvPhase& p)
 {
+    if (p.geo.fmt == MAK_FMT_MXFP4) return mak_gemv4_lds(p.geo.k, mak_gemv_nc(p.ncols));
     if (p.multi == 2) {
         const int64_t groups = (p.geo.n_rows + 16 * p.rr - 1) / (16 * p.rr);
         return mak_gemm16_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks);
@@ -578,6 +585,17 @@ int mak_gemm16_plan(const GemvPhase& p, int ncols, size_t lds_budget)
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
 {
     const int n_cu = device_cus();
+    if (p.geo.fmt == MAK_FMT_MXFP4) {
+        // 4-bit weights: k_gemv4, workgroups of 4 waves, one tile per wave
+        // up to 4096 workgroups (waves loop over the rest)
+        p.multi = 0;
+        p.ks = 1;
+        p.rr = p.geo.r;
+        p.jw = 1;
+        p.threads = MAK_BLOCK;
+        const int64_t wpb = MAK_BLOCK / 64;
+        return (int)std::max<int64_t>(1, std::min<int64_t>((p.geo.n_tiles + wpb - 1) / wpb, std::max(cap, 4096)));
+    }
     // (splitting one-column tiles over several waves with this kernel was
     // measured slower: its staging and combine cost more than the fold)
     p.multi = p.ncols >= 2;
@@ -815,6 +833,10 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
                     hipError_t e = set(f, bytes);
                     if (e != hipSuccess) return e;
                 }
+    {
+        hipError_t e = mak_gemv4_set_lds_limit(bytes_n);
+        if (e != hipSuccess) return e;
+    }
 #define X(D)                                                                               \
     {                                                                                      \
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D>),       \

@@ -164,6 +164,142 @@ void pack(const PackGeom& g, const RowSrc& src, std::vector<uint16_t>& out)
     }
 }
 
+}  // namespace
+
+extern "C" int mak_quantize_mxfp4(const uint16_t* w, int64_t rows, int32_t k, uint8_t* codes, uint8_t* scales);
+
+namespace {
+
+// Quantize each row (mak_quantize_mxfp4) and place its 16-byte code chunks
+// and scale bytes in slot order; padding rows are zero codes.
+int pack4(const PackGeom& g, const RowSrc& src, std::vector<uint8_t>& out)
+{
+    const int k = g.k, C = k / MAK_MX_BLOCK;
+    const int lr = 1 << g.lr_log2, G = 64 / lr, J = C / lr;
+    out.assign((size_t)g.bytes, 0);
+    std::vector<uint8_t> codes((size_t)k / 2), sc((size_t)C);
+    const int64_t rows_per_tile = (int64_t)G * g.r;
+    for (int64_t n = 0; n < g.n_rows; n++) {
+        const int rc = mak_quantize_mxfp4(src.row(n, k), 1, k, codes.data(), sc.data());
+        if (rc) return rc;
+        const int64_t tile = n / rows_per_tile;
+        const int rr = (int)(n - tile * rows_per_tile);
+        const int grp = rr / g.r, ri = rr % g.r;
+        for (int c = 0; c < C; c++) {
+            const int j = c / lr, sl = c % lr;
+            const int64_t slot = ((tile * J + j) * g.r + ri) * 64 + grp * lr + sl;
+            std::memcpy(&out[(size_t)slot * 16], &codes[(size_t)c * 16], 16);
+            out[(size_t)(g.scale_off + slot)] = sc[(size_t)c];
+        }
+    }
+    return MAK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit weights: OCP MXFP4 (Microscaling Formats specification v1.0).  A
+// block of 32 consecutive weights of a row shares the scale 2^e, stored as
+// the E8M0 byte e + 127, with e = floor(log2(block max |w|)) - 2 (2 being the
+// exponent of E2M1's largest value 6) clamped to [-127, 127] (-127 for an
+// all-zero block); each weight becomes the E2M1 code of w / 2^e rounded to
+// nearest, ties to the even code, saturating at 6; zero keeps a clear sign.
+// ---------------------------------------------------------------------------
+
+// floor(log2 |v|) of a nonzero finite bf16 magnitude (bits without the sign)
+int bf16_floor_log2(uint32_t mag)
+{
+    const uint32_t ef = mag >> 7;
+    if (ef) return (int)ef - 127;
+    return (31 - __builtin_clz(mag)) - 133;   // subnormal: mag * 2^-133
+}
+
+// E2M1 magnitude index (0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6) of |v| / 2^e.
+// With |v| = M * 2^E exactly (M the integer significand), 4|v|/2^e =
+// M * 2^(E - e + 2) is compared with the midpoints between neighbouring
+// magnitudes, times 4: 1, 3, 5, 7, 10, 14, 20.  At a midpoint the result is
+// the even index (mantissa bit 0): below at 1, 5, 10, 20, above at 3, 7, 14.
+uint32_t e2m1_index(uint32_t mag, int e)
+{
+    if (mag == 0) return 0;
+    const uint32_t ef = mag >> 7;
+    const uint64_t M = ef ? (0x80u | (mag & 0x7fu)) : mag;
+    const int E = (ef ? (int)ef : 1) - 134;
+    const int sh = E - e + 2;
+    static const uint64_t T[7] = {1, 3, 5, 7, 10, 14, 20};
+    uint32_t idx = 0;
+    for (int i = 0; i < 7; i++) {
+        int cmp;
+        if (sh >= 0) {
+            const uint64_t a = sh > 40 ? UINT64_MAX : (M << sh);
+            cmp = a > T[i] ? 1 : (a < T[i] ? -1 : 0);
+        } else if (-sh > 40) {
+            cmp = -1;
+        } else {
+            const uint64_t t = T[i] << (-sh);
+            cmp = M > t ? 1 : (M < t ? -1 : 0);
+        }
+        if (cmp > 0 || (cmp == 0 && (i & 1))) idx = (uint32_t)i + 1;
+        else break;
+    }
+    return idx;
+}
+
+// Lanes sharing one row of a 4-bit matrix.  A 4-bit chunk holds 32 inputs,
+// so lanes per row trade tiles against work per tile: at 64 lanes a K = 2048
+// row is one load per lane (many small tiles, each ending in a 64-lane
+// reduction), at 16 lanes four.  The layout takes the most lanes (<= 64,
+// dividing K/32) that leave at most 2048 tiles -- eight waves per CU on 256
+// CUs, all resident at once -- and otherwise the fewest.  Measured on the 1B
+// shape (us per launch, lanes 64/32/16): QKV 6.8/6.5/6.8, O 4.4/4.8/5.6,
+// gate/up 20.5/14.7/12.3, down 6.9/7.6/12.5 -- the rule picks 32, 64, 16, 64.
+// MAK_MXFP4_LANES (a power of two, 1..64) caps the lanes per row.
+int mxfp4_max_lanes()
+{
+    static int v = 0;
+    if (!v) {
+        const char* e = getenv("MAK_MXFP4_LANES");
+        const int x = e ? atoi(e) : 0;
+        v = (x >= 1 && x <= 64 && !(x & (x - 1))) ? x : 64;
+    }
+    return v;
+}
+
+constexpr int64_t kMxfp4MaxTiles = 2048;
+
+// rows per lane group of an [n, k] matrix with G groups per wave (make_geom's rule)
+int rows_per_group(int64_t n, int G, bool pairs)
+{
+    int r = pairs ? 2 : 1;
+    if ((n + (int64_t)G * 2 - 1) / ((int64_t)G * 2) >= 2048) r = 2;
+    return r;
+}
+
+// Geometry of a packed 4-bit [n, k] matrix (mak_internal.h): 16-byte chunks
+// of 32 codes, the row-group rule of make_geom.
+PackGeom make_geom4(int64_t n, int k, bool pairs)
+{
+    PackGeom g{};
+    g.n_rows = (int32_t)n;
+    g.k = k;
+    g.fmt = MAK_FMT_MXFP4;
+    const int C = k / MAK_MX_BLOCK;
+    int lr = gcd(C, mxfp4_max_lanes());
+    while (lr > 1) {
+        const int G = 64 / lr;
+        const int64_t rows_per_tile = (int64_t)G * rows_per_group(n, G, pairs);
+        if ((n + rows_per_tile - 1) / rows_per_tile <= kMxfp4MaxTiles) break;
+        lr >>= 1;
+    }
+    g.lr_log2 = ilog2(lr);
+    const int G = 64 / lr;
+    g.r = rows_per_group(n, G, pairs);
+    const int64_t rows_per_tile = (int64_t)G * g.r;
+    g.n_tiles = (int32_t)((n + rows_per_tile - 1) / rows_per_tile);
+    const int64_t slots = (int64_t)g.n_tiles * rows_per_tile * C;
+    g.scale_off = slots * 16;
+    g.bytes = (int64_t)align_up((size_t)(g.scale_off + slots));
+    return g;
+}
+
 struct LayerDev {
     size_t attn_norm, mlp_norm, q_norm, k_norm;
     size_t w_qkv, w_o, w_gu, w_down;
@@ -201,6 +337,11 @@ int validate_cfg(const mak_config* c)
     if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0f))
         return fail(MAK_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
     if (c->max_seq > (1 << 20)) return fail(MAK_EINVAL, "max_seq too large");
+    if (c->weight_format != MAK_WEIGHTS_BF16 && c->weight_format != MAK_WEIGHTS_MXFP4)
+        return fail(MAK_EINVAL, "weight_format must be MAK_WEIGHTS_BF16 or MAK_WEIGHTS_MXFP4");
+    if (c->weight_format == MAK_WEIGHTS_MXFP4 &&
+        (c->hidden % MAK_MX_BLOCK || c->intermediate % MAK_MX_BLOCK || (c->n_q_heads * c->head_dim) % MAK_MX_BLOCK))
+        return fail(MAK_EINVAL, "4-bit weights need hidden, intermediate and q_dim multiples of 32");
     const size_t attn_lds = mak_attn_lds_for(c->n_q_heads / c->n_kv_heads, c->head_dim,
                                              std::min(c->max_seq, kAttnSinglePassMax));
     if (attn_lds > (size_t)kAttnLdsBudget)
@@ -216,10 +357,11 @@ Layout make_layout(const mak_config* c)
     const int q_dim = c->n_q_heads * d, kv_dim = c->n_kv_heads * d;
     L.g_embed = make_geom(V, H, false);
     L.g_lm = L.g_embed;
-    L.g_qkv = make_geom(q_dim + 2 * kv_dim, H, false);
-    L.g_o = make_geom(H, q_dim, false);
-    L.g_gu = make_geom(2 * (int64_t)I, H, true);
-    L.g_down = make_geom(H, I, false);
+    auto geom = (c->weight_format == MAK_WEIGHTS_MXFP4) ? make_geom4 : make_geom;
+    L.g_qkv = geom(q_dim + 2 * kv_dim, H, false);
+    L.g_o = geom(H, q_dim, false);
+    L.g_gu = geom(2 * (int64_t)I, H, true);
+    L.g_down = geom(H, I, false);
     L.qkv_ld = q_dim + 2 * kv_dim;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -377,6 +519,14 @@ int collect_timing(mak_model* m)
     return MAK_OK;
 }
 
+// Largest column group whose fp32 inputs, staged in padded 32-input blocks
+// (36 floats each), fit the LDS budget of the 4-bit GEMV (at most 8).
+int max_cols_for_k4(int k)
+{
+    const int n = kLdsInputsN / ((k / MAK_MX_BLOCK) * 36 * 4);
+    return n >= 8 ? 8 : n >= 4 ? 4 : n >= 2 ? 2 : 1;
+}
+
 // Largest column group whose bf16 input rows fit the LDS budget.
 int max_cols_for_k(int k)
 {
@@ -393,8 +543,11 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
     // split the columns into groups whose inputs fit in LDS (the matrix-core
     // kernel stages at most 16 RMSNorm inputs of K <= 4096 and reads raw
     // inputs from memory: one launch)
-    const bool mfma = mak_gemm16_plan(p, ncols, kLdsBudgetN) != 0;
-    const int step = (p.epi == EPI_LOGITS || mfma) ? ncols : max_cols_for_k(p.geo.k);
+    const bool q4 = p.geo.fmt == MAK_FMT_MXFP4;
+    const bool mfma = !q4 && mak_gemm16_plan(p, ncols, kLdsBudgetN) != 0;
+    const int step = q4 ? max_cols_for_k4(p.geo.k)
+                        : (p.epi == EPI_LOGITS || mfma) ? ncols : max_cols_for_k(p.geo.k);
+    if (q4 && p.epi == EPI_LOGITS) return fail(MAK_EINVAL, "internal: 4-bit LM head");
     if (p.epi == EPI_LOGITS && !mfma && max_cols_for_k(p.geo.k) < ncols)
         return fail(MAK_EINVAL, "LM head input too wide for %d columns", ncols);
     for (int c0 = 0; c0 < ncols; c0 += step) {
@@ -405,8 +558,9 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
         if (q.epi == EPI_LOGITS && q.col0 != col0)
             return fail(MAK_EINVAL, "internal: LM head split");
         // host-side shape checks of what the kernel assumes
-        if (q.geo.k % 8 || q.ncols < 1 || q.ncols > MAK_MAX_COLS || q.col0 + q.ncols > MAK_MAX_COLS ||
-            mak_gemv_lds(q) > (size_t)(q.multi ? kLdsBudgetN : kLdsBudget) || q.n_blocks < 1 ||
+        if (q.geo.k % (q4 ? MAK_MX_BLOCK : 8) || q.ncols < 1 || q.ncols > MAK_MAX_COLS ||
+            q.col0 + q.ncols > MAK_MAX_COLS || (q4 && q.ncols > 8) ||
+            mak_gemv_lds(q) > (size_t)(q4 ? kLdsInputsN : q.multi ? kLdsBudgetN : kLdsBudget) || q.n_blocks < 1 ||
             (q.epi == EPI_SWIGLU && (q.geo.r % 2)) ||
             (q.multi && q.in_kind != IN_RAW && (q.geo.k >> 3) > MAK_NBLOCK))
             return fail(MAK_EINVAL, "internal: bad GEMV phase");
@@ -735,6 +889,37 @@ extern "C" {
 
 const char* mak_last_error(void) { return g_err.c_str(); }
 
+int mak_quantize_mxfp4(const uint16_t* w, int64_t rows, int32_t k, uint8_t* codes, uint8_t* scales)
+{
+    if (!w || !codes || !scales) return fail(MAK_EINVAL, "null pointer");
+    if (rows < 0 || k <= 0 || k % MAK_MX_BLOCK) return fail(MAK_EINVAL, "rows >= 0 and k a positive multiple of 32");
+    const int nb = k / MAK_MX_BLOCK;
+    // validate every weight first, so a failing call writes nothing
+    for (int64_t i = 0; i < rows * (int64_t)k; i++)
+        if (((w[i] >> 7) & 0xffu) == 0xffu)
+            return fail(MAK_EINVAL, "weight %lld (row %lld) is not finite", (long long)i, (long long)(i / k));
+    for (int64_t r = 0; r < rows; r++) {
+        for (int b = 0; b < nb; b++) {
+            const uint16_t* v = w + r * k + (int64_t)b * MAK_MX_BLOCK;
+            uint32_t amax = 0;
+            for (int i = 0; i < MAK_MX_BLOCK; i++) amax = std::max<uint32_t>(amax, v[i] & 0x7fffu);
+            int e = amax ? bf16_floor_log2(amax) - 2 : -127;
+            e = std::min(127, std::max(-127, e));
+            scales[r * nb + b] = (uint8_t)(e + 127);
+            uint8_t* out = codes + r * (k / 2) + (int64_t)b * (MAK_MX_BLOCK / 2);
+            for (int i = 0; i < MAK_MX_BLOCK; i += 2) {
+                uint32_t q[2];
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t idx = e2m1_index(v[i + h] & 0x7fffu, e);
+                    q[h] = idx | ((idx && (v[i + h] & 0x8000u)) ? 8u : 0u);
+                }
+                out[i / 2] = (uint8_t)(q[0] | (q[1] << 4));
+            }
+        }
+    }
+    return MAK_OK;
+}
+
 int mak_plan(const mak_config* cfg, size_t* arena_bytes)
 {
     int rc = validate_cfg(cfg);
@@ -780,7 +965,12 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
         HIP_TRY(hipStreamSynchronize(st));
         return MAK_OK;
     };
+    std::vector<uint8_t> buf4;
     auto put_packed = [&](size_t off, const PackGeom& g, const RowSrc& s) -> int {
+        if (g.fmt == MAK_FMT_MXFP4) {
+            if (const int e = pack4(g, s, buf4)) return e;
+            return put(off, buf4.data(), buf4.size());
+        }
         pack(g, s, buf);
         return put(off, buf.data(), buf.size() * 2);
     };

@@ -23,15 +23,27 @@
 // (j, ri, lane) holds chunk j*lr + s of row tile*g*r + group*r + ri.
 // Every wave load is therefore 64 lanes x 16 B = 1 KiB contiguous.  Rows past
 // N are zero padding.
+//
+// 4-bit matrices (fmt MAK_FMT_MXFP4, OCP MXFP4: K a multiple of 32): a 16-byte
+// chunk holds 32 consecutive inputs' E2M1 codes (two per byte, the lower
+// index in the low nibble), which are exactly one 32-weight block sharing one
+// E8M0 scale; C = K/32 chunks per row and the same slot order.  The scale
+// bytes follow the codes at byte offset scale_off, one per slot, in slot
+// order, so scale(slot) = base[scale_off + slot].
 // ---------------------------------------------------------------------------
+#define MAK_FMT_BF16 0
+#define MAK_FMT_MXFP4 1
+#define MAK_MX_BLOCK 32
+
 struct PackGeom {
     int32_t n_rows;    // N
     int32_t k;         // K
     int32_t lr_log2;   // log2(lanes per row)
     int32_t r;         // rows per lane group (1, 2 or 4)
     int32_t n_tiles;   // ceil(N / (g*r))
-    int32_t pad_;
-    int64_t bytes;     // packed size in bytes (n_tiles * g * r * K * 2)
+    int32_t fmt;       // MAK_FMT_BF16 or MAK_FMT_MXFP4
+    int64_t bytes;     // packed size in bytes (bf16: n_tiles*g*r*K*2; 4-bit: codes + scales)
+    int64_t scale_off; // 4-bit: byte offset of the scale bytes (= n_tiles*g*r*K/2)
 };
 
 // State of one column (one token being processed) of a step.

@@ -20,11 +20,12 @@ MAK_OK, MAK_EINVAL, MAK_ERANGE, MAK_ENOMEM, MAK_EDEVICE = 0, -1, -2, -3, -4
 MAK_MAX_BATCH = 16
 MAK_PREFILL_CHUNK = 8
 
-EXPORTS = ("mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_decode_step_static", "mak_generate",
+EXPORTS = ("mak_quantize_mxfp4", "mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_decode_step_static", "mak_generate",
            "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",
            "mak_set_attention_split", "mak_set_prefill_chunk", "mak_set_phase_timing",
            "mak_phase_times", "mak_free", "mak_last_error")
 EXEC_GRAPH, EXEC_PHASED = 0, 1
+WEIGHT_FORMATS = {"bf16": 0, "mxfp4": 1}
 PHASES = ("qkv", "attn", "o", "gateup", "down", "lmhead", "ctl")
 
 
@@ -41,7 +42,7 @@ class mak_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("tie_embeddings", ctypes.c_int32),
                 ("qk_norm", ctypes.c_int32), ("max_seq", ctypes.c_int32),
-                ("max_batch", ctypes.c_int32)]
+                ("max_batch", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 _P16 = ctypes.POINTER(ctypes.c_uint16)
@@ -71,6 +72,8 @@ def lib():
         import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I32 = ctypes.c_void_p, ctypes.c_int32
+        L.mak_quantize_mxfp4.argtypes = [P, ctypes.c_int64, I32, P, P]
+        L.mak_quantize_mxfp4.restype = ctypes.c_int
         L.mak_plan.argtypes = [ctypes.POINTER(mak_config), ctypes.POINTER(ctypes.c_size_t)]
         L.mak_load.argtypes = [ctypes.POINTER(mak_config), ctypes.POINTER(mak_weights), P,
                                ctypes.c_size_t, P, ctypes.POINTER(P)]
@@ -108,7 +111,20 @@ def make_config(shape, max_seq: Optional[int] = None, max_batch: Optional[int] =
                       shape.head_dim, shape.intermediate, shape.vocab, shape.rms_eps,
                       shape.rope_theta, int(shape.tie_embeddings), int(shape.qk_norm),
                       int(max_seq if max_seq is not None else shape.max_seq),
-                      int(max_batch if max_batch is not None else shape.max_batch))
+                      int(max_batch if max_batch is not None else shape.max_batch),
+                      WEIGHT_FORMATS[getattr(shape, "weight_format", "bf16")])
+
+
+def quantize_mxfp4(w_bits: np.ndarray):
+    """mak_quantize_mxfp4 on a [rows, k] uint16 bf16 matrix: returns
+    (codes [rows, k/2] uint8, two per byte, low nibble first; E8M0 scales
+    [rows, k/32] uint8).  Host only."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, k = w.shape
+    codes = np.zeros((rows, k // 2), np.uint8)
+    scales = np.zeros((rows, max(k // 32, 1)), np.uint8)
+    _check(lib().mak_quantize_mxfp4(w.ctypes.data, rows, k, codes.ctypes.data, scales.ctypes.data))
+    return codes, scales
 
 
 def plan(shape, max_seq=None, max_batch=None) -> int:

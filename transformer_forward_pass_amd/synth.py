@@ -43,6 +43,7 @@ class ModelShape:
     qk_norm: bool = False
     max_seq: int = 2048
     max_batch: int = 1
+    weight_format: str = "bf16"   # per-layer linear matrices: "bf16" or "mxfp4" (4-bit)
 
     @property
     def q_dim(self) -> int:
@@ -64,12 +65,15 @@ class ModelShape:
         return n
 
     def streamed_weight_bytes(self) -> int:
-        """bf16 bytes one decode token must read once: every layer weight,
-        the final norm and the LM head (the embedding row itself is 2*H)."""
+        """Bytes one decode token must read once: every layer weight, the
+        final norm and the LM head (the embedding row itself is 2*H).  With
+        4-bit weights each linear weight takes half a byte plus one scale
+        byte per 32 weights; norms and the LM head stay bf16."""
         H, I = self.hidden, self.intermediate
-        per_layer = (H * (self.q_dim + 2 * self.kv_dim) + self.q_dim * H
-                     + 3 * H * I + 2 * H + (2 * self.head_dim if self.qk_norm else 0))
-        return 2 * (self.n_layers * per_layer + H + self.vocab * H + H)
+        lin = H * (self.q_dim + 2 * self.kv_dim) + self.q_dim * H + 3 * H * I
+        norms = 2 * H + (2 * self.head_dim if self.qk_norm else 0)
+        lin_bytes = lin // 2 + lin // 32 if self.weight_format == "mxfp4" else 2 * lin
+        return self.n_layers * (lin_bytes + 2 * norms) + 2 * (H + self.vocab * H + H)
 
     def kv_bytes_per_position(self) -> int:
         """K and V bytes of one cached position over all layers (bf16)."""
@@ -116,6 +120,9 @@ WORKLOADS: Dict[str, Workload] = {
                                    prompt_len=16, max_new=128, batch=16, prompt_len_hi=256),
     # long-prompt prefill: a 2040-token prompt on the 1B shape, in chunks of 16
     "llama-3.2-1b-p2040": Workload(SHAPES["llama-3.2-1b"], prompt_len=2040, max_new=4, chunk=16),
+    # 4-bit (MXFP4) per-layer weights quantized from the same bf16 weights
+    "llama-3.2-1b-mxfp4": Workload(dataclasses.replace(SHAPES["llama-3.2-1b"], name="llama-3.2-1b-mxfp4",
+                                                       weight_format="mxfp4"), prompt_len=32, max_new=128),
 }
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
