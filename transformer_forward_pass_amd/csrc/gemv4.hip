@@ -116,11 +116,11 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv4(GemvPhase p)
     };
     uint4 bufA[QB], bufB[QB];
     uint32_t scA[QB], scB[QB];
+    finish_input<NC, true>(p, stg, hs, red, MAK_BLOCK);
     if (tile < p.geo.n_tiles) {
         load_res(tile);
         issue(bufA, scA, tile, 0);
     }
-    finish_input<NC, true>(p, stg, hs, red, MAK_BLOCK);
     __syncthreads();
 
     double acc[R][NC];

@@ -329,6 +329,17 @@ size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round);
 const void* mak_gemv4_fn(int r, int nc, int epi);
 size_t mak_gemv4_lds(int k, int nc);
 hipError_t mak_gemv4_set_lds_limit(int bytes);
+// gemv41.hip: the batch-1 4-bit GEMV with a compile-time tile shape
+const void* mak_gemv41_fn(int r, int j, int epi);
+hipError_t mak_gemv41_set_lds_limit(int bytes);
+
+// k_gemv41 for a one-column 4-bit phase (one tile per wave, so the grid
+// covers every tile), or nullptr
+static const void* gemv41_fn(const GemvPhase& p)
+{
+    if (p.ncols != 1 || p.geo.n_tiles > 4 * 16384) return nullptr;
+    return mak_gemv41_fn(p.geo.r, (p.geo.k / MAK_MX_BLOCK) >> p.geo.lr_log2, p.epi);
+}
 
 // Column capacity (template NC) for n active columns.
 int mak_gemv_nc(int ncols) { return ncols <= 1 ? 1 : ncols <= 2 ? 2 : ncols <= 4 ? 4 : ncols <= 8 ? 8 : 16; }
@@ -362,7 +373,10 @@ static bool gemv1_compiled(const GemvPhase& p) { return gemv1_fn_ks(p, 1) != nul
 
 static const void* gemv_fn(const GemvPhase& p)
 {
-    if (p.geo.fmt == MAK_FMT_MXFP4) return mak_gemv4_fn(p.geo.r, mak_gemv_nc(p.ncols), p.epi);
+    if (p.geo.fmt == MAK_FMT_MXFP4) {
+        if (const void* f = gemv41_fn(p)) return f;
+        return mak_gemv4_fn(p.geo.r, mak_gemv_nc(p.ncols), p.epi);
+    }
     if (p.multi == 2) return mak_gemm16_fn(p.rr, p.epi, p.in_kind != IN_RAW);
     if (p.multi) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
     if (const void* f = gemv1_fn(p)) return f;
@@ -594,6 +608,7 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
         p.jw = 1;
         p.threads = MAK_BLOCK;
         const int64_t wpb = MAK_BLOCK / 64;
+        if (gemv41_fn(p)) return (int)((p.geo.n_tiles + wpb - 1) / wpb);   // one tile per wave
         return (int)std::max<int64_t>(1, std::min<int64_t>((p.geo.n_tiles + wpb - 1) / wpb, std::max(cap, 4096)));
     }
     // (splitting one-column tiles over several waves with this kernel was
@@ -835,6 +850,8 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
                 }
     {
         hipError_t e = mak_gemv4_set_lds_limit(bytes_n);
+        if (e != hipSuccess) return e;
+        e = mak_gemv41_set_lds_limit(bytes_n);
         if (e != hipSuccess) return e;
     }
 #define X(D)                                                                               \

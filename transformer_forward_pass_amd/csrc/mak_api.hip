@@ -263,7 +263,17 @@ int mxfp4_max_lanes()
     return v;
 }
 
-constexpr int64_t kMxfp4MaxTiles = 2048;
+// most tiles of a 4-bit matrix layout (MAK_MXFP4_MAX_TILES overrides)
+int64_t mxfp4_max_tiles()
+{
+    static int64_t v = 0;
+    if (!v) {
+        const char* e = getenv("MAK_MXFP4_MAX_TILES");
+        const long x = e ? atol(e) : 0;
+        v = (x >= 64 && x <= (1 << 20)) ? x : 2048;
+    }
+    return v;
+}
 
 // rows per lane group of an [n, k] matrix with G groups per wave (make_geom's rule)
 int rows_per_group(int64_t n, int G, bool pairs)
@@ -286,7 +296,7 @@ PackGeom make_geom4(int64_t n, int k, bool pairs)
     while (lr > 1) {
         const int G = 64 / lr;
         const int64_t rows_per_tile = (int64_t)G * rows_per_group(n, G, pairs);
-        if ((n + rows_per_tile - 1) / rows_per_tile <= kMxfp4MaxTiles) break;
+        if ((n + rows_per_tile - 1) / rows_per_tile <= mxfp4_max_tiles()) break;
         lr >>= 1;
     }
     g.lr_log2 = ilog2(lr);
