@@ -432,7 +432,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the 1B-shape measurement")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the batched-decode and long-context measurements")
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, SECONDARY],
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, SECONDARY, "llama-3.2-1b-mxfp4"],
                     help="batch-1 workload of the main line (the other one goes to `secondary`)")
     ap.add_argument("--max-new", type=int, default=0,
                     help="override the greedy token count (short counter-collection runs only)")
@@ -463,7 +463,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4" if primary.endswith("mxfp4") else "bf16",
         "data": "synthetic",
         "config": {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of 8) + "
                                "%d greedy tokens, batch 1" % (primary, p0, n),
@@ -495,6 +495,7 @@ def main():
                                     "4-bit OCP MXFP4 (LM head bf16): 32-token prompt + 128 greedy tokens, "
                                     "batch 1",
                         "value": round(r4["tok_s"], 2), "unit": "tok/s",
+                        "dtype": "mxfp4 weights (E2M1 codes, E8M0 scale per 32), bf16 activations, f64 accumulation",
                         "ms_per_step": round(r4["ms_per_step"], 4),
                         "roofline": r4["roofline"], "token_roofline": r4["token_roofline"],
                         "phase_ms_per_step": r4["phase_ms_per_step"], "runs_ms": r4["runs_ms"]}
