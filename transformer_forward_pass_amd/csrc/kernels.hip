@@ -102,6 +102,34 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
             vpre[u] = *reinterpret_cast<const uint4*>(vc_h + (size_t)j * d + ch * 8);
         }
     }
+    if (!p.q_norm) {
+        // no qk-norm: rope straight from the loaded pairs (i, i + d/2) and
+        // their table entries, before the one barrier -- q at pos, the
+        // step's k rows at fp + ci; v rows as loaded
+        for (int t = tid; t < (1 + n_in) * half; t += kAttnBlock) {
+            const int vi = t / half, i = t - vi * half;
+            const int at = (vi == 0) ? pos : fp + vi - 1;
+            const float c = bf2f(p.cos_t[(size_t)at * half + i]);
+            const float sn = bf2f(p.sin_t[(size_t)at * half + i]);
+            const uint16_t* src = (vi == 0) ? p.qkv + (size_t)col * p.qkv_ld + h * d
+                                            : p.qkv + (size_t)(cs.first_col + vi - 1) * p.qkv_ld + q_dim + g * d;
+            const float a = bf2f(src[i]), b = bf2f(src[i + half]);
+            const float ra = rbf(rbf(a * c) - rbf(b * sn));
+            const float rb = rbf(rbf(b * c) + rbf(a * sn));
+            if (vi == 0) {
+                qf[i] = ra;
+                qf[i + half] = rb;
+            } else {
+                kin[(vi - 1) * d + i] = f2bf(ra);
+                kin[(vi - 1) * d + i + half] = f2bf(rb);
+            }
+        }
+        for (int t = tid; t < n_in * d; t += kAttnBlock) {
+            const int ci = t / d, i = t - ci * d;
+            vin[t] = p.qkv[(size_t)(cs.first_col + ci) * p.qkv_ld + q_dim + kv_dim + g * d + i];
+        }
+        __syncthreads();
+    } else {
     for (int t = tid; t < d; t += kAttnBlock) qf[t] = bf2f(p.qkv[(size_t)col * p.qkv_ld + h * d + t]);
     for (int t = tid; t < n_in * d; t += kAttnBlock) {
         const int ci = t / d, i = t - ci * d;
@@ -118,7 +146,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
     __syncthreads();
 
     // per-head qk RMSNorm (one wave per vector: q, then the step's k rows)
-    if (p.q_norm) {
+    {
         for (int vi = wave; vi < 1 + n_in; vi += kAttnWaves) {
             double ss = 0.0;
             for (int i = lane; i < d; i += 64) {
@@ -156,6 +184,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
         }
     }
     __syncthreads();
+    }
 
     // append this column's k', v at pos (single owner per kv group)
     if (owner) {
