@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
             const int ci = t / d, i = t - ci * d;
             vin[t] = p.qkv[(size_t)(cs.first_col + ci) * p.qkv_ld + q_dim + kv_dim + g * d + i];
         }
-        __syncthreads();
+        lds_barrier();
     } else {
     for (int t = tid; t < d; t += kAttnBlock) qf[t] = bf2f(p.qkv[(size_t)col * p.qkv_ld + h * d + t]);
     for (int t = tid; t < n_in * d; t += kAttnBlock) {
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
         rc[t] = p.cos_t[(size_t)at * half + i];
         rsn[t] = p.sin_t[(size_t)at * half + i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // per-head qk RMSNorm (one wave per vector: q, then the step's k rows)
     {
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // rope (pairs i, i + d/2): q at pos, the step's k rows at fp + ci
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
             kp[i + half] = f2bf(rbf(b * c) + rbf(a * sn));
         }
     }
-    __syncthreads();
+    lds_barrier();
     }
 
     // append this column's k', v at pos (single owner per kv group)
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
             if (ch == 0 && j < n) S[j] = rbf(rbf((float)a) * p.scale);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // softmax over the block: max, e_j = fp32(exp(sigma_j - max)),
     // Z = fp32(sum e_j), P_j = bf16(fp32(e_j / Z)); each thread rewrites only
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
         for (int j = tid; j < n; j += kAttnBlock) m = fmaxf(m, S[j]);
         m = wave_max(m);
         if (lane == 0) redf[wave] = m;
-        __syncthreads();
+        lds_barrier();
         m = redf[0];
         for (int w = 1; w < kAttnBlock / 64; w++) m = fmaxf(m, redf[w]);
         double z = 0.0;
@@ -257,10 +257,10 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
             S[j] = e;
             z += (double)e;
         }
-        const double Z = (double)(float)block_sum_rt(z, redd, kAttnBlock / 64);
+        const double Z = (double)(float)block_sum_lds(z, redd, kAttnBlock / 64);
         for (int j = tid; j < n; j += kAttnBlock) S[j] = rbf((float)((double)S[j] / Z));
     }
-    __syncthreads();
+    lds_barrier();
 
     // o = bf16(sum_j P_j V_j): per-lane partial sums over its rows, folded
     // within each 16-lane row (DPP), then the block's 4 * kAttnWaves rows through LDS
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
 #pragma unroll
         for (int e = 0; e < 8; e++) pv[grp16 * d + ch * 8 + e] = acc[e];
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < d; i += kAttnBlock) {
         double v = 0.0;
 #pragma unroll
