@@ -16,6 +16,9 @@ BIG = synth.small_shape(n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=2, head_
                         intermediate=688, vocab=5000)
 SMALL = synth.small_shape(n_layers=2, hidden=128, n_q_heads=4, n_kv_heads=1, head_dim=32,
                           intermediate=344, vocab=1000)
+# the same step with 4-bit (MXFP4) per-layer weights
+SMALL4 = synth.small_shape(n_layers=2, hidden=128, n_q_heads=4, n_kv_heads=1, head_dim=32,
+                           intermediate=352, vocab=1000, weight_format="mxfp4")
 
 
 def _ids(shape, n, seed):
@@ -33,8 +36,9 @@ def test_static_step_equals_decode_step_on_two_calls_in_a_row():
     assert torch.cuda.is_available(), "GPU test without a GPU"
     # first call: 300 cached positions with split-KV attention (scores,
     # chunk maxima and partial outputs in the static array); second: a
-    # smaller model at 9 positions through the single-pass attention
-    for shape, ctx, split, seed in ((BIG, 300, True, 5), (SMALL, 9, False, 6)):
+    # smaller model at 9 positions through the single-pass attention; third:
+    # a 4-bit model of that size
+    for shape, ctx, split, seed in ((BIG, 300, True, 5), (SMALL, 9, False, 6), (SMALL4, 9, False, 7)):
         a, b = _pair(shape, 512)
         prompt = _ids(shape, ctx, seed)
         la = a.prefill(prompt)
