@@ -650,9 +650,27 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             p.jw = 1;
             p.threads = MAK_NBLOCK;
             const int64_t groups = (p.geo.n_rows + 16 * rt - 1) / (16 * rt);
-            // (the LM head's argmax partials hold `cap` workgroups: its
-            // workgroups loop over the groups)
-            return (int)std::max<int64_t>(1, p.epi == EPI_LOGITS ? std::min<int64_t>(groups, cap) : groups);
+            // As many workgroups as are resident at once (the staged inputs
+            // take most of a CU's LDS): each stages its inputs once and loops
+            // over row groups, issuing the next group's first batch before
+            // reducing the current one.  (The LM head's argmax partials also
+            // hold at most `cap` workgroups.)  MAK_GEMM16_RESIDENT=0 launches
+            // one workgroup per row group instead.
+            static int res_env = -1;
+            if (res_env < 0) {
+                const char* e = getenv("MAK_GEMM16_RESIDENT");
+                res_env = (e && atoi(e) == 0) ? 0 : 1;
+            }
+            int64_t g = groups;
+            if (res_env) {
+                const bool staged = p.in_kind != IN_RAW;
+                // (LDS sized for several rounds: partial tiles beside the inputs)
+                const int occ = resident_blocks(mak_gemm16_fn(rt, p.epi, staged), MAK_NBLOCK,
+                                                mak_gemm16_lds(rt, p.geo.k, staged, false));
+                g = std::min<int64_t>(groups, (int64_t)occ * n_cu);
+            }
+            if (p.epi == EPI_LOGITS) g = std::min<int64_t>(g, cap);
+            return (int)std::max<int64_t>(1, g);
         }
         gemvn_plan(p, lds_budget_n, cap);
         p.threads = MAK_NBLOCK;
