@@ -38,12 +38,20 @@ namespace mak {
 
 typedef double d4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kG16Waves = 8;
-constexpr int kG16Block = kG16Waves * 64;
+// waves per workgroup: 16 for one row tile with RMSNorm inputs staged in LDS
+// (K split 16 ways: four waves per SIMD keep the matrix cores busy while the
+// staged inputs fill a CU's LDS, and each wave normalises one column), 8
+// otherwise (two or four tiles need the registers of two waves per SIMD;
+// with raw inputs, 16 waves measured slower: TinyLlama O 9.3 -> 10.6 us,
+// down 18.7 -> 21.0 us at 16 columns)
+__host__ __device__ constexpr int gemm16_waves(int rt, bool staged) { return (rt == 1 && staged) ? 16 : 8; }
 constexpr int kG16Slots = 17;   // LDS slots (16 bytes) per input chunk: 16 columns + 1 pad
 
 __host__ __device__ inline size_t gemm16_input_lds(int k) { return (size_t)(k >> 3) * kG16Slots * 16; }
-__host__ __device__ inline size_t gemm16_part_lds(int rt) { return (size_t)kG16Waves * rt * 4 * 64 * 8; }
+__host__ __device__ inline size_t gemm16_part_lds(int rt, bool staged)
+{
+    return (size_t)gemm16_waves(rt, staged) * rt * 4 * 64 * 8;
+}
 
 // 8 bf16 values of a 16-byte chunk as fp64
 __device__ __forceinline__ void chunk_f64(const uint4 v, double (&d)[8])
@@ -59,8 +67,9 @@ __device__ __forceinline__ void chunk_f64(const uint4 v, double (&d)[8])
 }
 
 template <int RT, int EPI, bool STAGED>
-__global__ __launch_bounds__(kG16Block, RT == 1 ? 4 : 2) void k_gemm16(GemvPhase p)
+__global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) void k_gemm16(GemvPhase p)
 {
+    constexpr int kG16Waves = gemm16_waves(RT, STAGED);
     constexpr int QB = 2;                   // 32-input blocks per batch (RT = 1: 4 waves per SIMD)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ float bval[kG16Waves][16];
@@ -139,8 +148,8 @@ __global__ __launch_bounds__(kG16Block, RT == 1 ? 4 : 2) void k_gemm16(GemvPhase
     };
 
     // 1. the first weight batch, then the input staging (RMSNorm inputs):
-    //    wave w normalises columns w and w + 8, one at a time; lane chunks
-    //    lane + 64*i.  The weights stay in flight throughout.
+    //    wave w normalises columns w, w + waves, ..., one at a time; lane
+    //    chunks lane + 64*i.  The weights stay in flight throughout.
     constexpr int SI = 8;                               // chunks per lane (K <= 4096)
     const int n_i = (C + 63) >> 6;
     int grp_idx = blockIdx.x;
@@ -150,8 +159,8 @@ __global__ __launch_bounds__(kG16Block, RT == 1 ? 4 : 2) void k_gemm16(GemvPhase
         const bool gather = p.in_kind == IN_GATHER_NORM;
         const uint4* nw = reinterpret_cast<const uint4*>(p.norm_w);
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int cw = wave + 8 * h;
+        for (int h = 0; h < 16 / kG16Waves; h++) {
+            const int cw = wave + kG16Waves * h;
             const bool active = cw < p.ncols;
             const int col = p.col0 + min(cw, p.ncols - 1);
             const uint4* base = gather ? reinterpret_cast<const uint4*>(p.embed)
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(kG16Block, RT == 1 ? 4 : 2) void k_gemm16(GemvPhase
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 double s = 0.0;
-#pragma unroll
+#pragma unroll 4
                 for (int w2 = 0; w2 < kG16Waves; w2++) s += part[((size_t)(w2 * RT + rt) * 4 + r) * 64 + lane];
                 y[r] = s;
             }
@@ -371,6 +380,10 @@ const void* mak_gemm16_fn(int rt, int epi, bool staged)
 // staged inputs' space)
 size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round)
 {
-    if (!staged) return gemm16_part_lds(rt);
-    return single_round ? std::max(gemm16_input_lds(k), gemm16_part_lds(rt)) : gemm16_input_lds(k) + gemm16_part_lds(rt);
+    if (!staged) return gemm16_part_lds(rt, false);
+    return single_round ? std::max(gemm16_input_lds(k), gemm16_part_lds(rt, true))
+                        : gemm16_input_lds(k) + gemm16_part_lds(rt, true);
 }
+
+// workgroup size of k_gemm16 with rt row tiles (staged: RMSNorm inputs)
+int mak_gemm16_threads(int rt, bool staged) { return gemm16_waves(rt, staged) * 64; }

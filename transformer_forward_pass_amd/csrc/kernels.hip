@@ -353,6 +353,7 @@ static const void* gemv_fn_r1(int epi)
 // gemm16.hip: the multi-column GEMM on the fp64 matrix cores
 const void* mak_gemm16_fn(int rt, int epi, bool staged);
 size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round);
+int mak_gemm16_threads(int rt, bool staged);
 
 // gemv4.hip: the GEMV over 4-bit (MXFP4) weights
 const void* mak_gemv4_fn(int r, int nc, int epi);
@@ -648,7 +649,7 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             p.multi = 2;
             p.rr = rt;
             p.jw = 1;
-            p.threads = MAK_NBLOCK;
+            p.threads = mak_gemm16_threads(rt, p.in_kind != IN_RAW);
             const int64_t groups = (p.geo.n_rows + 16 * rt - 1) / (16 * rt);
             // As many workgroups as are resident at once (the staged inputs
             // take most of a CU's LDS): each stages its inputs once and loops
@@ -665,7 +666,7 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             if (res_env) {
                 const bool staged = p.in_kind != IN_RAW;
                 // (LDS sized for several rounds: partial tiles beside the inputs)
-                const int occ = resident_blocks(mak_gemm16_fn(rt, p.epi, staged), MAK_NBLOCK,
+                const int occ = resident_blocks(mak_gemm16_fn(rt, p.epi, staged), p.threads,
                                                 mak_gemm16_lds(rt, p.geo.k, staged, false));
                 g = std::min<int64_t>(groups, (int64_t)occ * n_cu);
             }
