@@ -210,6 +210,19 @@ int mak_set_executor(mak_model *m, int executor);
  * 0 always splits.  Returns MAK_EINVAL for a negative threshold. */
 int mak_set_attention_split(mak_model *m, int32_t above);
 
+/* Prompt-chunk attention past the split threshold.  A prefill step's
+ * columns are consecutive positions of one sequence, so with on = 1 (the
+ * default) its split-KV attention runs blockwise: one workgroup per (query
+ * head, chunk of 128 positions) reads that chunk's K rows, then its V rows,
+ * once for all columns of the step and applies each column's causal limit;
+ * each (column, head) softmax row is computed once ("CuTeDSL at Perplexity",
+ * section on prefill and decode specialization: a prefill variant with its
+ * own grid and block assignment).  With
+ * on = 0 each column runs the per-column split-KV kernels.  Both give
+ * bitwise-identical results; decode and batched steps are unaffected.
+ * Returns MAK_EINVAL unless on is 0 or 1. */
+int mak_set_block_attention(mak_model *m, int32_t on);
+
 /* Prompt tokens per prefill step, 1..16 (default MAK_PREFILL_CHUNK = 8).  The
  * "model-as-a-kernel" page consumes prompts in chunks of up to eight tokens,
  * bitwise identical to token-by-token consumption (Method section).  Larger

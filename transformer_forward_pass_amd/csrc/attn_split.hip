@@ -243,8 +243,17 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn_pv(AttnPhase p)
     m = redf[0];
     for (int w = 1; w < MAK_BLOCK / 64; w++) m = fmaxf(m, redf[w]);
     const float* sc = p.sc + ((size_t)col * Hq + h) * p.max_seq;
+    // each thread sums j = tid, tid + MAK_BLOCK, ... in that order, its loads
+    // issued eight at a time
     double z = 0.0;
-    for (int j = tid; j < n; j += MAK_BLOCK) z += (double)(float)exp((double)sc[j] - (double)m);
+    for (int b = tid; b < n; b += 8 * MAK_BLOCK) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = (b + u * MAK_BLOCK < n) ? sc[b + u * MAK_BLOCK] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (b + u * MAK_BLOCK < n) z += (double)(float)exp((double)v[u] - (double)m);
+    }
     const double Z = (double)(float)block_sum_rt(z, redd, MAK_BLOCK / 64);
     for (int j = j0 + tid; j < j1; j += MAK_BLOCK) {
         const float e = (float)exp((double)sc[j] - (double)m);
@@ -299,8 +308,16 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn_combine(AttnPhase p)
     const int n_used = (n + MAK_ATTN_CHUNK - 1) / MAK_ATTN_CHUNK;
     const double* op = p.opart + ((size_t)col * Hq + h) * p.n_chunks * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        // chunks summed in order, their loads issued eight at a time
         double v = 0.0;
-        for (int c = 0; c < n_used; c++) v += op[(size_t)c * d + i];
+        for (int c0 = 0; c0 < n_used; c0 += 8) {
+            double x[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) x[u] = (c0 + u < n_used) ? op[(size_t)(c0 + u) * d + i] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (c0 + u < n_used) v += x[u];
+        }
         p.o[(size_t)col * Hq * d + h * d + i] = f2bf((float)v);
     }
 }

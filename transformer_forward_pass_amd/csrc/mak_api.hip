@@ -27,6 +27,8 @@
 hipError_t mak_launch_gemv(const GemvPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 hipError_t mak_launch_attn_split(const AttnPhase& p, int stage, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+// attn_block.hip
+hipError_t mak_launch_attn_block(const AttnPhase& p, int stage, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 hipError_t mak_launch_set_ctl(Ctl* ctl, const ColState* cols, int ncols, int step, hipStream_t st, hipEvent_t e0,
                               hipEvent_t e1);
 hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes);
@@ -452,8 +454,10 @@ struct PhaseTiming {
 };
 
 // Attention kernel of a step: the single pass over an LDS score row (up to
-// 4096 positions), or split-KV.
-enum AttnMode { ATTN_SINGLE = 1, ATTN_SPLIT = 2 };
+// 4096 positions), split-KV, or blockwise split-KV (a prompt chunk: every
+// column of one sequence, each chunk of K and V rows read once for all of
+// them).
+enum AttnMode { ATTN_SINGLE = 1, ATTN_SPLIT = 2, ATTN_BLOCK = 3 };
 
 // A captured step: (ncols, lm_begin, lm_count, attention mode) -> executable graph.
 struct StepGraph {
@@ -469,6 +473,7 @@ struct mak_model {
     bool use_graphs = true;
     int prefill_chunk = MAK_PREFILL_CHUNK;   // prompt tokens per prefill step (<= MAK_MAX_COLS)
     int split_above = 0;                 // split-KV attention once pos + 1 exceeds this
+    bool block_attn = true;              // prompt chunks past split_above run blockwise
     std::vector<StepGraph> graphs;
     Layout L;
     char* arena;
@@ -642,7 +647,14 @@ int record_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_
         a.n_chunks = L.n_chunks;
         a.s_cap = L.s_cap;
         if (mak_attn_lds(a) > (size_t)kAttnLdsBudget) return fail(MAK_EINVAL, "internal: attention LDS");
-        if (attn == ATTN_SPLIT) {
+        if (attn == ATTN_BLOCK) {
+            for (int stage = 0; stage < 4; stage++)
+                if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
+                         return stage < 3 ? mak_launch_attn_block(a, stage, m->cur, e0, e1)
+                                          : mak_launch_attn_split(a, 2, m->cur, e0, e1);
+                     })))
+                    return rc;
+        } else if (attn == ATTN_SPLIT) {
             for (int stage = 0; stage < 3; stage++)
                 if ((rc = launch(m, MAK_PHASE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
                          return mak_launch_attn_split(a, stage, m->cur, e0, e1);
@@ -746,7 +758,9 @@ int check_graph(hipGraph_t graph)
 // phase timing is on.  The step reads its per-call state (tokens, positions,
 // slots) from the control block, so one graph serves every step of a shape.
 // max_n = the largest pos + 1 among the step's columns: above the model's
-// threshold (or past the single-pass capacity) attention runs split-KV.
+// threshold (or past the single-pass capacity) attention runs split-KV,
+// blockwise when the step is a prompt chunk (one_seq: columns are the
+// consecutive positions of one sequence).
 StepScratch arena_scratch(const mak_model* m)
 {
     const Layout& L = m->L;
@@ -755,15 +769,18 @@ StepScratch arena_scratch(const mak_model* m)
 }
 
 // Attention kernel for a step whose longest context is max_n positions:
-// split-KV above the model's threshold or past the single-pass capacity.
-int attn_mode(const mak_model* m, int max_n)
+// split-KV above the model's threshold or past the single-pass capacity,
+// blockwise for a prompt chunk of two or more columns.
+int attn_mode(const mak_model* m, int max_n, int ncols = 1, bool one_seq = false)
 {
-    return (max_n > m->split_above || max_n > m->L.s_cap) ? ATTN_SPLIT : ATTN_SINGLE;
+    if (max_n <= m->split_above && max_n <= m->L.s_cap) return ATTN_SINGLE;
+    return (one_seq && ncols >= 2 && m->block_attn) ? ATTN_BLOCK : ATTN_SPLIT;
 }
 
-int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, int max_n)
+int run_step(mak_model* m, int ncols, int lm_begin, int lm_count, int32_t* d_out_tokens, int max_n,
+             bool one_seq = false)
 {
-    const int attn = attn_mode(m, max_n);
+    const int attn = attn_mode(m, max_n, ncols, one_seq);
     const StepScratch sc = arena_scratch(m);
     if (!m->use_graphs || m->tm.on) {
         m->cur = m->stream;
@@ -825,7 +842,8 @@ int prefill_chunks(mak_model* m, int slot, const int32_t* ids, int n, int start_
         int rc = set_cols(m, cols, T, step0);
         if (rc) return rc;
         const bool last = c0 + T >= n;
-        rc = run_step(m, T, T - 1, (last && want_lm) ? 1 : 0, m->at<int32_t>(m->L.out_tokens), start_pos + c0 + T);
+        rc = run_step(m, T, T - 1, (last && want_lm) ? 1 : 0, m->at<int32_t>(m->L.out_tokens), start_pos + c0 + T,
+                      true);
         if (rc) return rc;
     }
     return MAK_OK;
@@ -1101,6 +1119,15 @@ int mak_set_attention_split(mak_model* m, int32_t above)
     if (rc) return rc;
     if (above < 0) return fail(MAK_EINVAL, "split threshold %d < 0", above);
     m->split_above = above;
+    return MAK_OK;
+}
+
+int mak_set_block_attention(mak_model* m, int32_t on)
+{
+    int rc = check_model(m);
+    if (rc) return rc;
+    if (on != 0 && on != 1) return fail(MAK_EINVAL, "block attention switch %d is not 0 or 1", on);
+    m->block_attn = on != 0;
     return MAK_OK;
 }
 

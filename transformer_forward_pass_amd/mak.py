@@ -22,7 +22,7 @@ MAK_PREFILL_CHUNK = 8
 
 EXPORTS = ("mak_quantize_mxfp4", "mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_decode_step_static", "mak_generate",
            "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",
-           "mak_set_attention_split", "mak_set_prefill_chunk", "mak_set_phase_timing",
+           "mak_set_attention_split", "mak_set_block_attention", "mak_set_prefill_chunk", "mak_set_phase_timing",
            "mak_phase_times", "mak_free", "mak_last_error")
 EXEC_GRAPH, EXEC_PHASED = 0, 1
 WEIGHT_FORMATS = {"bf16": 0, "mxfp4": 1}
@@ -88,6 +88,7 @@ def lib():
         L.mak_set_executor.argtypes = [P, ctypes.c_int]
         L.mak_set_attention_split.argtypes = [P, I32]
         L.mak_set_prefill_chunk.argtypes = [P, I32]
+        L.mak_set_block_attention.argtypes = [P, I32]
         L.mak_set_phase_timing.argtypes = [P, ctypes.c_int]
         L.mak_phase_times.argtypes = [P, P, P]
         L.mak_free.argtypes = [P]
@@ -251,6 +252,10 @@ class MakModel:
     def set_attention_split(self, above: int):
         """Split-KV attention once a step's largest pos + 1 exceeds `above` (0: always)."""
         _check(lib().mak_set_attention_split(self.h, int(above)))
+
+    def set_block_attention(self, on: bool):
+        """Blockwise split-KV attention for prompt chunks (on by default)."""
+        _check(lib().mak_set_block_attention(self.h, int(on)))
 
     def set_prefill_chunk(self, tokens: int):
         """Prompt tokens per prefill step (1..16; 8 by default)."""
