@@ -436,6 +436,8 @@ def main():
                     help="batch-1 workload of the main line (the other one goes to `secondary`)")
     ap.add_argument("--max-new", type=int, default=0,
                     help="override the greedy token count (short counter-collection runs only)")
+    ap.add_argument("--only", choices=["batched", "batched16", "long_context", "long_prefill"],
+                    help="run one of the secondary measurements alone and print its JSON (kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -446,6 +448,13 @@ def main():
     if not os.path.exists(mak.LIB_PATH):
         from transformer_forward_pass_amd import build as B
         B.build()
+    if args.only:
+        one = {"batched": lambda: measure_batched(args),
+               "batched16": lambda: measure_batched(args, "tinyllama-1.1b-b16"),
+               "long_context": lambda: measure_long(args),
+               "long_prefill": lambda: measure_long_prefill(args)}[args.only]
+        print(json.dumps({args.only: one()}))
+        return
     primary = args.workload
     other = SECONDARY if primary == WORKLOAD else WORKLOAD
     r = measure(args, primary, args.steps)

@@ -18,7 +18,7 @@
 //      head of each kv group), then per column (one wave each) the scores
 //      sigma_j = bf16(bf16(q'.K_j) * scale) -> global scratch, chunk maximum;
 //   S  k_attn_blk_softmax (column, head): max over the chunk maxima,
-//      Z = fp32(sum_j fp32(exp(sigma_j - max))), P_j = bf16(fp32(e_j / Z))
+//      Z = fp32(sum_j fp32(exp(sigma_j - max))), P_j = bf16(e_j / Z)
 //      written over the scores, once per row;
 //   B  k_attn_blk_pv      (head, chunk): the chunk's V rows into LDS, per
 //      column (one wave each) o_c = sum_j P_j V_j in fp64 -> global scratch;
@@ -299,11 +299,13 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_softmax(AttnPhase p)
         for (int u = 0; u < kSoftBatch; u++)
             if (b + u * kBlkThreads < n) z += (double)(float)exp((double)v[u] - (double)m);
     }
-    const double Z = (double)(float)block_sum_lds(z, redd, kBlkWaves);
+    // (e / Z below: the correctly rounded fp32 division, equal to the fp64
+    // quotient rounded to fp32)
+    const float Z = (float)block_sum_lds(z, redd, kBlkWaves);
     // (each thread rewrites only the entries it read)
 #pragma unroll
     for (int u = 0; u < kSoftBatch; u++)
-        if (tid + u * kBlkThreads < n) sc[tid + u * kBlkThreads] = rbf((float)((double)e0[u] / Z));
+        if (tid + u * kBlkThreads < n) sc[tid + u * kBlkThreads] = rbf(e0[u] / Z);
     for (int b = tid + SB; b < n; b += SB) {
         float v[kSoftBatch];
 #pragma unroll
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_softmax(AttnPhase p)
         for (int u = 0; u < kSoftBatch; u++)
             if (b + u * kBlkThreads < n) {
                 const float e = (float)exp((double)v[u] - (double)m);
-                sc[b + u * kBlkThreads] = rbf((float)((double)e / Z));
+                sc[b + u * kBlkThreads] = rbf(e / Z);
             }
     }
 }

@@ -13,7 +13,7 @@
 //      sigma_j = bf16(bf16(q'.K_j) * scale) -> global scratch, chunk maximum;
 //   B  k_attn_pv      (column, query head, chunk): global max over the chunk
 //      maxima, Z = fp32(sum_j fp32(exp(sigma_j - max))) over all positions,
-//      P_j = bf16(fp32(e_j / Z)) for the chunk, partial o_c = sum_j P_j V_j
+//      P_j = bf16(e_j / Z) for the chunk, partial o_c = sum_j P_j V_j
 //      in fp64 -> global scratch;
 //   C  k_attn_combine (column, query head): o = bf16(fp32(sum_c o_c)), chunks
 //      in order.
@@ -254,10 +254,12 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_attn_pv(AttnPhase p)
         for (int u = 0; u < 8; u++)
             if (b + u * MAK_BLOCK < n) z += (double)(float)exp((double)v[u] - (double)m);
     }
-    const double Z = (double)(float)block_sum_rt(z, redd, MAK_BLOCK / 64);
+    // (e / Z: the correctly rounded fp32 division, equal to the fp64 quotient
+    // rounded to fp32)
+    const float Z = (float)block_sum_rt(z, redd, MAK_BLOCK / 64);
     for (int j = j0 + tid; j < j1; j += MAK_BLOCK) {
         const float e = (float)exp((double)sc[j] - (double)m);
-        pc[j - j0] = rbf((float)((double)e / Z));
+        pc[j - j0] = rbf(e / Z);
     }
     __syncthreads();
 

@@ -225,21 +225,26 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
     lds_barrier();
 
     // softmax over the block: max, e_j = fp32(exp(sigma_j - max)),
-    // Z = fp32(sum e_j), P_j = bf16(fp32(e_j / Z)); each thread rewrites only
-    // the entries it reads
-    if (n <= 256) {   // a short row: one wave, no extra barriers
+    // Z = fp32(sum e_j), P_j = bf16(e_j / Z) with the correctly rounded fp32
+    // division (the fp64 quotient of two fp32 values rounded to fp32 is that
+    // same value); each thread rewrites only the entries it reads
+    if (n <= 256) {   // a short row: one wave, no extra barriers, four entries per lane
         if (wave == 0) {
-            float m = -INFINITY;
-            for (int j = lane; j < n; j += 64) m = fmaxf(m, S[j]);
+            float sv[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) sv[u] = (lane + 64 * u < n) ? S[lane + 64 * u] : -INFINITY;
+            float m = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
             m = wave_max(m);
             double z = 0.0;
-            for (int j = lane; j < n; j += 64) {
-                const float e = (float)exp((double)S[j] - (double)m);
-                S[j] = e;
-                z += (double)e;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                sv[u] = (float)exp((double)sv[u] - (double)m);
+                if (lane + 64 * u < n) z += (double)sv[u];
             }
-            const double Z = (double)(float)wave_sum(z);
-            for (int j = lane; j < n; j += 64) S[j] = rbf((float)((double)S[j] / Z));
+            const float Z = (float)wave_sum(z);
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if (lane + 64 * u < n) S[lane + 64 * u] = rbf(sv[u] / Z);
         }
     } else {
         __shared__ float redf[kAttnBlock / 64];
@@ -257,8 +262,8 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
             S[j] = e;
             z += (double)e;
         }
-        const double Z = (double)(float)block_sum_lds(z, redd, kAttnBlock / 64);
-        for (int j = tid; j < n; j += kAttnBlock) S[j] = rbf((float)((double)S[j] / Z));
+        const float Z = (float)block_sum_lds(z, redd, kAttnBlock / 64);
+        for (int j = tid; j < n; j += kAttnBlock) S[j] = rbf(S[j] / Z);
     }
     lds_barrier();
 
