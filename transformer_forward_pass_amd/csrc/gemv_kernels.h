@@ -227,13 +227,22 @@ __device__ __forceinline__ void argmax_tail(const GemvPhase& p, const float* bes
     for (int c = wave; c < p.ncols; c += NW) {
         float v = -INFINITY;
         int i = 0x7fffffff;
-        for (int b = lane; b < p.n_blocks; b += 64) {
-            const float v2 = p.part_val[b * MAK_MAX_COLS + c];
-            const int i2 = p.part_idx[b * MAK_MAX_COLS + c];
-            if (v2 > v || (v2 == v && i2 < i)) {
-                v = v2;
-                i = i2;
+        // sixteen partials per lane in flight at once (1024 blocks in one batch)
+        for (int b0 = lane; b0 < p.n_blocks; b0 += 16 * 64) {
+            float vv[16];
+            int ii[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                const int b = b0 + 64 * u;
+                vv[u] = (b < p.n_blocks) ? p.part_val[b * MAK_MAX_COLS + c] : -INFINITY;
+                ii[u] = (b < p.n_blocks) ? p.part_idx[b * MAK_MAX_COLS + c] : 0x7fffffff;
             }
+#pragma unroll
+            for (int u = 0; u < 16; u++)
+                if (vv[u] > v || (vv[u] == v && ii[u] < i)) {
+                    v = vv[u];
+                    i = ii[u];
+                }
         }
         for (int o = 32; o > 0; o >>= 1) {
             const float v2 = __shfl_xor(v, o, 64);
