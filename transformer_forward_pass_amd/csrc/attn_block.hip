@@ -48,6 +48,9 @@ struct BlkGeom {
     static_assert(PASSES * RW == MAK_ATTN_CHUNK && PASSES % 4 == 0, "chunk must be whole groups of 4 passes");
     static_assert(UK >= 1 && UK * kBlkThreads == MAK_ATTN_CHUNK * LP, "chunk must be whole loads");
     static_assert(MAK_MAX_COLS * LP <= kBlkThreads, "one 16-byte piece of the step's rows per thread");
+    // K rows in LDS are padded by 16 bytes, so the scores' one-row-per-lane
+    // 16-byte reads of eight consecutive rows fall in distinct banks
+    static constexpr int KSD = D + 8;
 };
 
 // P values staged per thread by the P.V kernel: every column's chunk row
@@ -93,14 +96,14 @@ __device__ __forceinline__ void load_chunk(const uint16_t* cache_h, const BlkRan
 
 // Only the cached rows go to LDS: the rows past them belong to the step and
 // are written by other threads.
-template <int D>
+template <int D, int STRIDE>
 __device__ __forceinline__ void store_chunk(uint16_t* lds, const BlkRange& r, const uint4 (&v)[BlkGeom<D>::UK])
 {
     constexpr int LP = BlkGeom<D>::LP;
 #pragma unroll
     for (int u = 0; u < BlkGeom<D>::UK; u++) {
-        const int i = threadIdx.x + u * kBlkThreads;
-        if (r.j0 + i / LP < r.cend) reinterpret_cast<uint4*>(lds)[i] = v[u];
+        const int i = threadIdx.x + u * kBlkThreads, row = i / LP, q = i - row * LP;
+        if (r.j0 + row < r.cend) reinterpret_cast<uint4*>(lds + row * STRIDE)[q] = v[u];
     }
 }
 
@@ -111,9 +114,11 @@ template <int D>
 __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_scores(AttnPhase p)
 {
     using Gm = BlkGeom<D>;
-    constexpr int d = D, half = D / 2, LP = Gm::LP;
-    __shared__ __attribute__((aligned(16))) uint16_t ks[MAK_ATTN_CHUNK * D];   // K rows j0 .. j1-1
-    __shared__ __attribute__((aligned(16))) float qs[MAK_MAX_COLS * D];         // the columns' q'
+    constexpr int d = D, half = D / 2, LP = Gm::LP, KSD = Gm::KSD;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[MAK_ATTN_CHUNK * KSD];  // K rows j0 .. j1-1 (padded)
+    __shared__ __attribute__((aligned(16))) float qs[MAK_MAX_COLS * D];         // the columns' q (norm, rope)
+    __shared__ __attribute__((aligned(16))) double qd[MAK_MAX_COLS * D];        // q' in fp64
+    __shared__ float redm[kBlkWaves][8];                                         // per-wave column maxima
     __shared__ __attribute__((aligned(16))) uint16_t rc[MAK_MAX_COLS * half];   // rope rows fp .. fp+T-1
     __shared__ __attribute__((aligned(16))) uint16_t rs[MAK_MAX_COLS * half];
 
@@ -148,14 +153,14 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_scores(AttnPhase p)
     const uint4 cv = rope_ld ? *reinterpret_cast<const uint4*>(p.cos_t + roff) : zero4();
     const uint4 sv = rope_ld ? *reinterpret_cast<const uint4*>(p.sin_t + roff) : zero4();
 
-    store_chunk<D>(ks, r, kr);
+    store_chunk<D, KSD>(ks, r, kr);
     if (qi < r.T) {
         const uint32_t u[4] = {qv.x, qv.y, qv.z, qv.w};
         float* qp = qs + qi * d + qq * 8;
 #pragma unroll
         for (int e = 0; e < 8; e++) qp[e] = (e & 1) ? bf_hi(u[e >> 1]) : bf_lo(u[e >> 1]);
     }
-    if (qi < r.n_s) reinterpret_cast<uint4*>(ks + (r.s0 - r.j0 + qi) * d)[qq] = kv;
+    if (qi < r.n_s) reinterpret_cast<uint4*>(ks + (r.s0 - r.j0 + qi) * KSD)[qq] = kv;
     if (rope_ld) {
         reinterpret_cast<uint4*>(rc + ri * half)[rq] = cv;
         reinterpret_cast<uint4*>(rs + ri * half)[rq] = sv;
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_scores(AttnPhase p)
     const int nv = r.T + r.n_s;
     if (p.q_norm) {
         for (int vi = wave; vi < nv; vi += kBlkWaves) {
-            uint16_t* kp = ks + (r.s0 - r.j0 + vi - r.T) * d;
+            uint16_t* kp = ks + (r.s0 - r.j0 + vi - r.T) * KSD;
             double ss = 0.0;
             for (int e = lane; e < d; e += 64) {
                 const double x = (vi < r.T) ? (double)qs[vi * d + e] : (double)bf2f(kp[e]);
@@ -188,12 +193,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_scores(AttnPhase p)
         const float cf = bf2f(rc[at * half + e]);
         const float sf = bf2f(rs[at * half + e]);
         if (vi < r.T) {
-            float* qp = qs + vi * d;
+            const float* qp = qs + vi * d;
             const float a = qp[e], b = qp[e + half];
-            qp[e] = rbf(rbf(a * cf) - rbf(b * sf));
-            qp[e + half] = rbf(rbf(b * cf) + rbf(a * sf));
+            qd[vi * d + e] = (double)rbf(rbf(a * cf) - rbf(b * sf));
+            qd[vi * d + e + half] = (double)rbf(rbf(b * cf) + rbf(a * sf));
         } else {
-            uint16_t* kp = ks + (r.s0 - r.j0 + vi - r.T) * d;
+            uint16_t* kp = ks + (r.s0 - r.j0 + vi - r.T) * KSD;
             const float a = bf2f(kp[e]), b = bf2f(kp[e + half]);
             kp[e] = f2bf(rbf(a * cf) - rbf(b * sf));
             kp[e + half] = f2bf(rbf(b * cf) + rbf(a * sf));
@@ -204,50 +209,68 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_scores(AttnPhase p)
     // 3. KV append of the step's rows in this chunk (one head per kv group)
     if (owner && qi < r.n_s) {
         const size_t at = (head_base + r.s0 + qi) * d + qq * 8;
-        *reinterpret_cast<uint4*>(p.kc + at) = reinterpret_cast<const uint4*>(ks + (r.s0 - r.j0 + qi) * d)[qq];
+        *reinterpret_cast<uint4*>(p.kc + at) = reinterpret_cast<const uint4*>(ks + (r.s0 - r.j0 + qi) * KSD)[qq];
         *reinterpret_cast<uint4*>(p.vc + at) = vv;
     }
 
-    // 4. scores: wave w takes columns w, w + 4, ...; column t sees positions
-    //    < fp + t + 1.  Four passes at a time: four independent dot products
-    //    per lane in flight (rows past the limit read stale LDS, never kept).
-    const int sub = lane >> Gm::LPL, ch = lane & (LP - 1);
-    for (int t = wave; t < r.T; t += kBlkWaves) {
-        const int je = min(r.j1, r.fp + t + 1);
-        if (r.j0 >= je) continue;
-        double qreg[8];
+    // 4. scores: thread i owns row i % 128 of the chunk and computes whole dot
+    //    products (elements in order, one fp64 chain per column) for the
+    //    columns of its half: half 0 (waves 0-1) takes the first ceil(T/2)
+    //    columns, half 1 the rest.  The q' values are the same for every lane
+    //    of a wave (broadcast LDS reads); column t keeps rows < fp + t + 1.
+    {
+        const int row = tid & (MAK_ATTN_CHUNK - 1), hh = tid >> 7;
+        const int cpg = (r.T + 1) >> 1;
+        const int t0 = hh * cpg, nt = min(cpg, r.T - t0);   // (wave-uniform)
+        const int j = r.j0 + row;
+        double acc[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) qreg[e] = (double)qs[t * d + ch * 8 + e];
-        float* sc = p.sc + ((size_t)t * Hq + h) * p.max_seq;
-        float mloc = -INFINITY;
-        for (int u0 = 0; u0 < Gm::PASSES; u0 += 4) {
-            if (r.j0 + u0 * Gm::RW >= je) break;           // wave-uniform
-            uint4 kk[4];
+        for (int tt = 0; tt < 8; tt++) acc[tt] = 0.0;
+        if (nt > 0) {
+            const uint4* krow = reinterpret_cast<const uint4*>(ks + row * KSD);
 #pragma unroll
-            for (int k = 0; k < 4; k++) kk[k] = reinterpret_cast<const uint4*>(ks + ((u0 + k) * Gm::RW + sub) * d)[ch];
-            double a[4];
+            for (int q = 0; q < LP; q++) {
+                const uint4 kk = krow[q];
+                const uint32_t ku[4] = {kk.x, kk.y, kk.z, kk.w};
+                double kd[8];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t ku[4] = {kk[k].x, kk[k].y, kk[k].z, kk[k].w};
-                a[k] = 0.0;
+                for (int e = 0; e < 8; e++) kd[e] = (double)((e & 1) ? bf_hi(ku[e >> 1]) : bf_lo(ku[e >> 1]));
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    a[k] = fma(qreg[e], (double)((e & 1) ? bf_hi(ku[e >> 1]) : bf_lo(ku[e >> 1])), a[k]);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; k++) a[k] = group_sum<Gm::LPL>(a[k]);
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const int j = r.j0 + (u0 + k) * Gm::RW + sub;
-                if (j < je) {
-                    const float s = rbf(rbf((float)a[k]) * p.scale);
-                    if (ch == 0) sc[j] = s;
-                    mloc = fmaxf(mloc, s);
+                for (int tt = 0; tt < 8; tt++) {
+                    if (tt < nt) {
+                        const double2* qp = reinterpret_cast<const double2*>(qd + (t0 + tt) * d + q * 8);
+                        const double2 q0 = qp[0], q1 = qp[1], q2 = qp[2], q3 = qp[3];
+                        acc[tt] = fma(q0.x, kd[0], acc[tt]);
+                        acc[tt] = fma(q0.y, kd[1], acc[tt]);
+                        acc[tt] = fma(q1.x, kd[2], acc[tt]);
+                        acc[tt] = fma(q1.y, kd[3], acc[tt]);
+                        acc[tt] = fma(q2.x, kd[4], acc[tt]);
+                        acc[tt] = fma(q2.y, kd[5], acc[tt]);
+                        acc[tt] = fma(q3.x, kd[6], acc[tt]);
+                        acc[tt] = fma(q3.y, kd[7], acc[tt]);
+                    }
                 }
             }
         }
-        mloc = wave_max(mloc);
-        if (lane == 0) p.cmax[((size_t)t * Hq + h) * p.n_chunks + c] = mloc;
+#pragma unroll
+        for (int tt = 0; tt < 8; tt++) {
+            float m = -INFINITY;
+            if (tt < nt) {
+                const int t = t0 + tt;
+                if (j < min(r.j1, r.fp + t + 1)) {
+                    const float sv2 = rbf(rbf((float)acc[tt]) * p.scale);
+                    p.sc[((size_t)t * Hq + h) * p.max_seq + j] = sv2;
+                    m = sv2;
+                }
+            }
+            m = wave_max(m);
+            if (lane == 0) redm[wave][tt] = m;
+        }
+    }
+    lds_barrier();
+    if (tid < r.T) {
+        const int t = tid, cpg = (r.T + 1) >> 1, hh = t >= cpg, tt = t - hh * cpg;
+        p.cmax[((size_t)t * Hq + h) * p.n_chunks + c] = fmaxf(redm[2 * hh][tt], redm[2 * hh + 1][tt]);
     }
 }
 
@@ -354,53 +377,63 @@ __global__ __launch_bounds__(kBlkThreads) void k_attn_blk_pv(AttnPhase p)
         const int i = tid + u * kBlkThreads, t = i / MAK_ATTN_CHUNK, j = r.j0 + (i - t * MAK_ATTN_CHUNK);
         pl[u] = (t < r.T && j < min(r.j1, r.fp + t + 1)) ? p.sc[((size_t)t * Hq + h) * p.max_seq + j] : 0.0f;
     }
-    store_chunk<D>(vs, r, vr);
+    store_chunk<D, D>(vs, r, vr);
     if (qi < r.n_s) reinterpret_cast<uint4*>(vs + (r.s0 - r.j0 + qi) * d)[qq] = sv;
 #pragma unroll
     for (int u = 0; u < kBlkPLoads; u++) ps[tid + u * kBlkThreads] = pl[u];
     lds_barrier();
 
+    // wave w accumulates its columns t = w + 4i (i < 4) together: each V
+    // piece is converted once for all of them.  Per column the sums run in
+    // pass order; rows past a column's limit have P = 0, rows past the
+    // chunk's end (stale LDS) a zeroed V.
     const int sub = lane >> Gm::LPL, ch = lane & (LP - 1);
-    for (int t = wave; t < r.T; t += kBlkWaves) {
-        const int je = min(r.j1, r.fp + t + 1);
-        if (r.j0 >= je) continue;
-        const float* pr = ps + t * MAK_ATTN_CHUNK;
-        double acc[8];
+    const int nw = (r.T - wave + kBlkWaves - 1) / kBlkWaves;   // this wave's columns (wave-uniform)
+    if (nw > 0) {
+        const int je_w = min(r.j1, r.fp + wave + kBlkWaves * (nw - 1) + 1);   // its last column's limit
+        double acc[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) acc[e] = 0.0;
-        // four passes at a time, summed in pass order; rows past the limit
-        // have P = 0 and their (stale) V zeroed
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[i][e] = 0.0;
         for (int u0 = 0; u0 < Gm::PASSES; u0 += 4) {
-            if (r.j0 + u0 * Gm::RW >= je) break;           // wave-uniform
-            double pj[4];
-            uint4 vv[4];
+            if (r.j0 + u0 * Gm::RW >= je_w) break;         // wave-uniform
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 const int jj = (u0 + k) * Gm::RW + sub;
-                const bool in = r.j0 + jj < je;
-                pj[k] = in ? (double)pr[jj] : 0.0;
-                vv[k] = reinterpret_cast<const uint4*>(vs + jj * d)[ch];
-                if (!in) vv[k] = zero4();
-            }
+                uint4 vv = reinterpret_cast<const uint4*>(vs + jj * d)[ch];
+                if (r.j0 + jj >= r.j1) vv = zero4();
+                const uint32_t vu[4] = {vv.x, vv.y, vv.z, vv.w};
+                double vd[8];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t vu[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+                for (int e = 0; e < 8; e++) vd[e] = (double)((e & 1) ? bf_hi(vu[e >> 1]) : bf_lo(vu[e >> 1]));
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    acc[e] = fma(pj[k], (double)((e & 1) ? bf_hi(vu[e >> 1]) : bf_lo(vu[e >> 1])), acc[e]);
+                for (int i = 0; i < 4; i++) {
+                    if (i < nw) {
+                        const double pj = (double)ps[(wave + kBlkWaves * i) * MAK_ATTN_CHUNK + jj];
+#pragma unroll
+                        for (int e = 0; e < 8; e++) acc[i][e] = fma(pj, vd[e], acc[i][e]);
+                    }
+                }
             }
         }
         // sum over the wave's row groups (lanes with the same piece ch)
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            double v = acc[e];
-            for (int off = LP; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-            acc[e] = v;
-        }
-        if (sub == 0) {
-            double* op = p.opart + (((size_t)t * Hq + h) * p.n_chunks + c) * d + ch * 8;
+        for (int i = 0; i < 4; i++) {
+            if (i >= nw) continue;
+            const int t = wave + kBlkWaves * i;
+            if (r.j0 >= min(r.j1, r.fp + t + 1)) continue;   // (wave-uniform) the column does not reach this chunk
 #pragma unroll
-            for (int e = 0; e < 8; e++) op[e] = acc[e];
+            for (int e = 0; e < 8; e++) {
+                double v = acc[i][e];
+                for (int off = LP; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+                acc[i][e] = v;
+            }
+            if (sub == 0) {
+                double* op = p.opart + (((size_t)t * Hq + h) * p.n_chunks + c) * d + ch * 8;
+#pragma unroll
+                for (int e = 0; e < 8; e++) op[e] = acc[i][e];
+            }
         }
     }
 }
