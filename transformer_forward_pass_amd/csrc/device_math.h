@@ -19,13 +19,18 @@ __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u <<
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f2bf(float f)
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN (sign
+// and leading payload kept).  gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32): over every fp32 bit pattern it gives exactly the
+// integer rounding (u + 0x7fff + bit 16) >> 16, NaN -> (u >> 16) | 0x40.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two values in one conversion: lo in bits 0-15, hi in bits 16-31
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // value of f rounded to bf16
@@ -290,6 +295,13 @@ __device__ __forceinline__ float rms_scale(double ss, int n, float eps)
 __device__ __forceinline__ uint16_t rms_apply(float x, float r, float w)
 {
     return f2bf(w * rbf(x * r));
+}
+
+// two normalised elements (the bf16 pair u, weights ww) packed as a bf16 pair
+__device__ __forceinline__ uint32_t rms_apply2(uint32_t u, float r, uint32_t ww)
+{
+    const uint32_t t = f2bf2(bf_lo(u) * r, bf_hi(u) * r);
+    return f2bf2(bf_lo(ww) * bf_lo(t), bf_hi(ww) * bf_hi(t));
 }
 
 }  // namespace mak

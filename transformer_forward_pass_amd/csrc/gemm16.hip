@@ -158,53 +158,66 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) voi
     if constexpr (STAGED) {
         const bool gather = p.in_kind == IN_GATHER_NORM;
         const uint4* nw = reinterpret_cast<const uint4*>(p.norm_w);
+        // the norm weight is loaded once per workgroup (thread i: chunk i)
+        // into the pad slot of each staged chunk; every wave then reads it
+        // from LDS instead of loading all K of it for each of its columns
+        const bool w_ld = (int)threadIdx.x < C;
+        const uint4 wv = w_ld ? nw[threadIdx.x] : make_uint4(0, 0, 0, 0);
+        uint4 sv[16 / kG16Waves][SI];
+        double ss[16 / kG16Waves];
 #pragma unroll
         for (int h = 0; h < 16 / kG16Waves; h++) {
             const int cw = wave + kG16Waves * h;
-            const bool active = cw < p.ncols;
             const int col = p.col0 + min(cw, p.ncols - 1);
             const uint4* base = gather ? reinterpret_cast<const uint4*>(p.embed)
                                        : reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
             const int token = gather ? p.ctl->cols[col].token : 0;
-            uint4 sv[SI], sw[SI];
 #pragma unroll
             for (int i = 0; i < SI; i++) {
                 if (i < n_i) {
                     const int q = min(lane + 64 * i, C - 1);
-                    sv[i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
-                    sw[i] = nw[q];
+                    sv[h][i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
                 }
             }
-            double ss = 0.0;
+        }
+        if (w_ld) hsT[threadIdx.x * kG16Slots + 16] = wv;
+#pragma unroll
+        for (int h = 0; h < 16 / kG16Waves; h++) {
+            double a2 = 0.0;
 #pragma unroll
             for (int i = 0; i < SI; i++) {
                 if (i < n_i && lane + 64 * i < C) {
-                    const uint32_t u[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
+                    const uint32_t u[4] = {sv[h][i].x, sv[h][i].y, sv[h][i].z, sv[h][i].w};
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const double a = bf_lo(u[e]), b = bf_hi(u[e]);
-                        ss = fma(a, a, ss);
-                        ss = fma(b, b, ss);
+                        const double x0 = bf_lo(u[e]), x1 = bf_hi(u[e]);
+                        a2 = fma(x0, x0, a2);
+                        a2 = fma(x1, x1, a2);
                     }
                 }
             }
-            ss = wave_sum(ss);
-            const float rs = rms_scale(ss, K, p.eps);
+            ss[h] = wave_sum(a2);
+        }
+        lds_barrier();   // the norm weight in LDS (the weight batch stays in flight)
+#pragma unroll
+        for (int h = 0; h < 16 / kG16Waves; h++) {
+            const int cw = wave + kG16Waves * h;
+            const bool active = cw < p.ncols;
+            const float rs = rms_scale(ss[h], K, p.eps);
             const bool store_x = active && p.in_kind == IN_GATHER_NORM && blockIdx.x == 0;
             uint4* xs = reinterpret_cast<uint4*>(p.x_store + (size_t)(p.col0 + cw) * p.x_ld);
 #pragma unroll
             for (int i = 0; i < SI; i++) {
                 const int q = lane + 64 * i;
                 if (i < n_i && q < C) {
-                    if (store_x) xs[q] = sv[i];
-                    const uint32_t u[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
-                    const uint32_t ww[4] = {sw[i].x, sw[i].y, sw[i].z, sw[i].w};
+                    if (store_x) xs[q] = sv[h][i];
+                    const uint4 sw = hsT[q * kG16Slots + 16];
+                    const uint32_t u[4] = {sv[h][i].x, sv[h][i].y, sv[h][i].z, sv[h][i].w};
+                    const uint32_t ww[4] = {sw.x, sw.y, sw.z, sw.w};
                     uint32_t o[4];
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const uint32_t lo = rms_apply(bf_lo(u[e]), rs, bf_lo(ww[e]));
-                        const uint32_t hi = rms_apply(bf_hi(u[e]), rs, bf_hi(ww[e]));
-                        o[e] = lo | (hi << 16);
+                        o[e] = rms_apply2(u[e], rs, ww[e]);
                     }
                     hsT[q * kG16Slots + cw] =
                         active ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);

@@ -156,9 +156,7 @@ __device__ __forceinline__ void finish_input(const GemvPhase& p, Staged<NC>& st,
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const uint32_t lo = rms_apply(bf_lo(u[e]), r, bf_lo(ww[e]));
-                    const uint32_t hi = rms_apply(bf_hi(u[e]), r, bf_hi(ww[e]));
-                    o[e] = lo | (hi << 16);
+                    o[e] = rms_apply2(u[e], r, ww[e]);
                 }
                 store_chunk_f32(hc + stage_off<PAD32>(q), make_uint4(o[0], o[1], o[2], o[3]));
             }

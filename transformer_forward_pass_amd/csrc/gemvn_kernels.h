@@ -134,9 +134,7 @@ __device__ __forceinline__ void finish_inputs_n(const GemvPhase& p, const Staged
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const uint32_t lo = rms_apply(bf_lo(u[e]), rs, bf_lo(ww[e]));
-                    const uint32_t hi = rms_apply(bf_hi(u[e]), rs, bf_hi(ww[e]));
-                    o[e] = lo | (hi << 16);
+                    o[e] = rms_apply2(u[e], rs, ww[e]);
                 }
                 hs4[cw * C + q] = keep_or_zero(active, make_uint4(o[0], o[1], o[2], o[3]));
             }
