@@ -15,13 +15,15 @@
 //   A  k_attn_blk_scores  (head, chunk): the chunk's cached K rows and the
 //      step's own k rows (qk-norm, rope at their positions) into LDS, the
 //      columns' q (qk-norm, rope) into LDS, the step rows' KV append (first
-//      head of each kv group), then per column (one wave each) the scores
+//      head of each kv group), then each thread owns one row and computes
+//      whole dot products for the columns of its half of the workgroup:
 //      sigma_j = bf16(bf16(q'.K_j) * scale) -> global scratch, chunk maximum;
 //   S  k_attn_blk_softmax (column, head): max over the chunk maxima,
 //      Z = fp32(sum_j fp32(exp(sigma_j - max))), P_j = bf16(e_j / Z)
 //      written over the scores, once per row;
-//   B  k_attn_blk_pv      (head, chunk): the chunk's V rows into LDS, per
-//      column (one wave each) o_c = sum_j P_j V_j in fp64 -> global scratch;
+//   B  k_attn_blk_pv      (head, chunk): the chunk's V rows and every
+//      column's P into LDS; wave w accumulates o_c = sum_j P_j V_j in fp64
+//      for its columns t = w (mod 4) together -> global scratch;
 //   C  k_attn_combine (attn_split.hip): chunks summed in order, bf16.
 //
 // The arithmetic is the split-KV kernels' (products exact in fp64, sums
