@@ -160,3 +160,32 @@ def test_block_launches_per_prompt_step():
     with pytest.raises(mak.MakError):
         m.set_block_attention(2)
     m.free()
+
+
+@pytest.mark.parametrize("case", ["ragged-max-seq", "gqa8", "past-4096"])
+def test_block_edges_equal_per_column_split(torch_cuda, case):
+    """Edges of the (head, 128-position chunk) grid: a max_seq that is not a
+    multiple of 128 (the last chunk ragged, the prompt ending in it), eight
+    query heads per kv head (one KV-append owner among eight), and a prompt
+    running past the 4096-position single-pass capacity.  Blockwise ==
+    per-column split bitwise, logits and KV cache."""
+    if case == "ragged-max-seq":
+        s, n, max_seq, chunk = SHAPES["d32-gqa3"], 290, 300, 16
+    elif case == "gqa8":
+        s = synth.small_shape(n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=32,
+                              intermediate=344, vocab=600)
+        n, max_seq, chunk = 333, 512, 13
+    else:
+        s = synth.small_shape(n_layers=1, hidden=128, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                              intermediate=256, vocab=300)
+        n, max_seq, chunk = 4200, 4224, 16
+    w = synth.make_weights(s)
+    ids = _ids(s, n, seed=9)
+    print("case", case, flush=True)
+    blk = _model(s, w, True, chunk, max_seq=max_seq)
+    col = _model(s, w, False, chunk, max_seq=max_seq)
+    a, b = _np(blk.prefill(ids)), _np(col.prefill(ids))
+    assert np.array_equal(a, b), case
+    _same_kv(blk, col, s, n, case)
+    blk.free()
+    col.free()
