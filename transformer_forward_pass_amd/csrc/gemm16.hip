@@ -141,7 +141,7 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) voi
             const int kb = kb0 + min(bt * QB + q, max(nkb - 1, 0));
             const int c = min(4 * kb + kg, C - 1);
 #pragma unroll
-            for (int rt = 0; rt < RT; rt++) buf[q * (RT + 1) + rt] = W[a_addr(rt, c)];
+            for (int rt = 0; rt < RT; rt++) buf[q * (RT + 1) + rt] = ld_stream16(&W[a_addr(rt, c)]);
             if constexpr (STAGED) buf[q * (RT + 1) + RT] = make_uint4(0, 0, 0, 0);
             else buf[q * (RT + 1) + RT] = xin[c];
         }

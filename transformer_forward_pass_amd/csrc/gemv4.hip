@@ -84,8 +84,8 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv4(GemvPhase p)
 #pragma unroll
         for (int i = 0; i < QB; i++)
             if (i < n) {
-                buf[i] = *reinterpret_cast<const uint4*>(wt + (lane * 16 + i * 1024));
-                sc[i] = st[lane + i * 64];
+                buf[i] = ld_stream16(wt + (lane * 16 + i * 1024));
+                sc[i] = ld_stream_u8(st + lane + i * 64);
             }
     };
     // wait for a batch (codes and scales) and keep later loads below

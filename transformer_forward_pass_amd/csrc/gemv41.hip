@@ -75,12 +75,12 @@ __global__ __launch_bounds__(MAK_BLOCK) void k_gemv41(GemvPhase p)
     uint4 buf[QT];
 #pragma unroll
     for (int i = 0; i < QT; i++) {
-        sc[i] = S[i * 64];
+        sc[i] = ld_stream_u8(S + i * 64);
         asm volatile("" ::: "memory");
     }
 #pragma unroll
     for (int i = 0; i < QT; i++) {
-        buf[i] = W[i * 64];
+        buf[i] = ld_stream16(&W[i * 64]);
         asm volatile("" ::: "memory");
     }
 

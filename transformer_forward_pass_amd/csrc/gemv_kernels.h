@@ -329,7 +329,7 @@ __global__ __launch_bounds__(MAK_GBLOCK) void k_gemv(GemvPhase p)
         const int n = min(QB, Q - b * QB);
 #pragma unroll
         for (int i = 0; i < QB; i++)
-            if (i < n) buf[i] = *reinterpret_cast<const uint4*>(wt + (lane_off + (uint32_t)i * 1024u));
+            if (i < n) buf[i] = ld_stream16(wt + (lane_off + (uint32_t)i * 1024u));
     };
 
     int tile = blockIdx.x * (MAK_GBLOCK / 64) + wave;
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(gemv1_waves(R, J) * 64) void k_gemv1(GemvPhase p)
         for (int i = 0; i < QH; i++) {
             const int c = i / R;
             const int jj = (KS == 2) ? min(half * JH + c, J - 1) : c;
-            buf[i] = *reinterpret_cast<const uint4*>(wt + lane_off + (jj * R + (i - c * R)) * 1024);
+            buf[i] = ld_stream16(wt + lane_off + (jj * R + (i - c * R)) * 1024);
             asm volatile("" ::: "memory");
         }
     };

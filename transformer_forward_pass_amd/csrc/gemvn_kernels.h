@@ -293,7 +293,7 @@ __global__ __launch_bounds__(MAK_NBLOCK) void k_gemvn(GemvPhase p)
             for (int u = 0; u < RR; u++) {
                 const int64_t t = min((int64_t)g * TU + (u >> rl), (int64_t)n_tiles - 1);
                 const int ri = u & (R - 1);
-                buf[ub * RR + u] = W[((t * J + j) * R + ri) * 64 + lane];
+                buf[ub * RR + u] = ld_stream16(&W[((t * J + j) * R + ri) * 64 + lane]);
             }
             if (++ij == UW) {
                 ij = 0;
