@@ -1,7 +1,7 @@
 """Greedy-decode benchmark on one MI355X.
 
 One step = one mak_generate call of the SmolLM2-135M-shaped random-init model:
-a 32-token prompt consumed in chunks of 8, then 128 greedy tokens at batch 1
+a 32-token prompt consumed in chunks of 16, then 128 greedy tokens at batch 1
 with on-device token feedback -- every phase of the decode path (embedding
 gather, RMSNorm, Q/K/V/O and SwiGLU GEMVs, rope, GQA attention over the KV
 cache, LM head, argmax).  value = generated tokens per second over the K
@@ -124,6 +124,7 @@ def run_gpu(args, shape, wl, w, prompt, steps):
     import torch
     from transformer_forward_pass_amd import mak
     m = mak.MakModel(shape, w, device="cuda:0", max_seq=shape.max_seq)
+    m.set_prefill_chunk(wl.chunk)
     max_new = wl.max_new
     for _ in range(args.warmup):
         m.generate(prompt, max_new)
@@ -178,7 +179,7 @@ def measure(args, name, steps):
     dom = max(kinds, key=lambda k: times[k][0])
     avg_s = times[dom][0] / times[dom][1] / 1e3
     if dom == "attn":
-        tot, launches = _attn_bytes(shape, p0, n)
+        tot, launches = _attn_bytes(shape, p0, n, wl.chunk)
         per_launch = tot // launches
     else:
         per_launch = _gemv_bytes(shape, dom)
@@ -316,8 +317,9 @@ def measure_batched(args, name="tinyllama-1.1b", reps=2):
 
 
 def measure_long(args, name="qwen3-0.6b", reps=2):
-    """Long context: a 512-token prompt in 64 chunks of 8, then 256 greedy
-    tokens (attention runs split-KV past 384 positions at head_dim 128)."""
+    """Long context: a 512-token prompt in 64 chunks of 8 (the workload's
+    chunk), then 256 greedy tokens (attention runs split-KV past 384
+    positions at head_dim 128)."""
     import torch
     from transformer_forward_pass_amd import mak, synth
     wl = synth.WORKLOADS[name]
@@ -325,6 +327,7 @@ def measure_long(args, name="qwen3-0.6b", reps=2):
     w = synth.make_weights(shape)
     prompt = synth.make_prompts(wl)[0]
     m = mak.MakModel(shape, w, device="cuda:0", max_seq=shape.max_seq)
+    m.set_prefill_chunk(wl.chunk)
     m.generate(prompt, 8)
     torch.cuda.synchronize()
     best = bestp = None
@@ -359,9 +362,9 @@ def measure_long(args, name="qwen3-0.6b", reps=2):
     p0, n = len(prompt), wl.max_new
     avg_ctx = p0 + n / 2.0
     tok_bytes = shape.streamed_weight_bytes() + shape.kv_bytes_per_position() * avg_ctx
-    prefill_bytes = (p0 // 8) * shape.streamed_weight_bytes() * 1.0
-    return {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of 8) + %d greedy tokens, "
-                        "batch 1" % (name, p0, n),
+    prefill_bytes = (p0 // wl.chunk) * shape.streamed_weight_bytes() * 1.0
+    return {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of %d) + %d greedy tokens, "
+                        "batch 1" % (name, p0, wl.chunk, n),
             "value": round(n / best, 2), "unit": "tok/s",
             "decode_tok_s": round(1.0 / t_dec, 2), "prefill_ms": round(bestp * 1e3, 3),
             "token_roofline": {"bytes_per_token": int(tok_bytes),
@@ -474,8 +477,8 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4" if primary.endswith("mxfp4") else "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of 8) + "
-                               "%d greedy tokens, batch 1" % (primary, p0, n),
+        "config": {"workload": "%s-shaped random-init decoder: %d-token prompt (chunks of %d) + "
+                               "%d greedy tokens, batch 1" % (primary, p0, wl.chunk, n),
                    "accumulate": "f64"},
         "roofline": r["roofline"],
         "token_roofline": r["token_roofline"],
@@ -484,8 +487,8 @@ def main():
     }
     if not args.no_secondary:
         r2 = measure(args, other, max(2, args.steps // 2))
-        out["secondary"] = {"workload": "%s-shaped random-init decoder: 32-token prompt + 128 greedy "
-                                        "tokens, batch 1" % other,
+        out["secondary"] = {"workload": "%s-shaped random-init decoder: 32-token prompt (chunks of %d) + "
+                                        "128 greedy tokens, batch 1" % (other, r2["wl"].chunk),
                             "value": round(r2["tok_s"], 2), "unit": "tok/s",
                             "ms_per_step": round(r2["ms_per_step"], 4),
                             "roofline": r2["roofline"], "token_roofline": r2["token_roofline"],
@@ -501,8 +504,8 @@ def main():
         progress("long-prompt prefill done")
         r4 = measure(args, "llama-3.2-1b-mxfp4", max(2, args.steps // 2))
         out["mxfp4"] = {"workload": "llama-3.2-1b-shaped random-init decoder, per-layer linear weights in "
-                                    "4-bit OCP MXFP4 (LM head bf16): 32-token prompt + 128 greedy tokens, "
-                                    "batch 1",
+                                    "4-bit OCP MXFP4 (LM head bf16): 32-token prompt (chunks of %d) + "
+                                    "128 greedy tokens, batch 1" % r4["wl"].chunk,
                         "value": round(r4["tok_s"], 2), "unit": "tok/s",
                         "dtype": "mxfp4 weights (E2M1 codes, E8M0 scale per 32), bf16 activations, f64 accumulation",
                         "ms_per_step": round(r4["ms_per_step"], 4),

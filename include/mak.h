@@ -47,7 +47,7 @@ extern "C" {
 #define MAK_EDEVICE (-4)  /* HIP runtime error (message kept for mak_last_error)     */
 
 #define MAK_MAX_BATCH 16    /* columns of one decode batch                          */
-#define MAK_PREFILL_CHUNK 8 /* prompts are consumed in chunks of at most 8 tokens    */
+#define MAK_PREFILL_CHUNK 16 /* prompts are consumed in chunks of at most 16 tokens */
 
 /* Weight formats of the per-layer linear matrices (q, k, v, o, gate, up,
  * down).  The embedding, the LM head and the norm weights stay bf16.
@@ -223,11 +223,13 @@ int mak_set_attention_split(mak_model *m, int32_t above);
  * Returns MAK_EINVAL unless on is 0 or 1. */
 int mak_set_block_attention(mak_model *m, int32_t on);
 
-/* Prompt tokens per prefill step, 1..16 (default MAK_PREFILL_CHUNK = 8).  The
+/* Prompt tokens per prefill step, 1..16 (default MAK_PREFILL_CHUNK = 16).  The
  * "model-as-a-kernel" page consumes prompts in chunks of up to eight tokens,
  * bitwise identical to token-by-token consumption (Method section).  Larger
  * chunks stream each layer's weights once for more tokens and stay bitwise
  * identical, since every dot product is exact before its single rounding.
+ * Steps of 9..16 tokens run on the fp64 matrix cores and take about as long
+ * as a step of 8 on the vector units, hence the default.
  * Returns MAK_EINVAL outside 1..16. */
 int mak_set_prefill_chunk(mak_model *m, int32_t tokens);
 

@@ -65,6 +65,7 @@ def _load(name, max_batch=None):
     w = synth.make_weights(wl.shape)
     assert synth.weights_digest(w) == g["weights_sha256"], "weight generator drifted"
     m = mak.MakModel(wl.shape, w, max_batch=max_batch)
+    m.set_prefill_chunk(wl.chunk)           # the workload's prompt chunk
     return g, full, wl, m
 
 

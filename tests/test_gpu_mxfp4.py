@@ -54,12 +54,14 @@ def _ids(shape, n, seed=1):
     return [int(t) for t in np.random.default_rng(seed).integers(0, shape.vocab, n)]
 
 
+@pytest.mark.parametrize("chunk", [8, 16])
 @pytest.mark.parametrize("name", sorted(Q4))
-def test_mxfp4_shapes_teacher_forced(torch_cuda, orc, name):
+def test_mxfp4_shapes_teacher_forced(torch_cuda, orc, name, chunk):
     s = Q4[name]
-    print("case", name, flush=True)
+    print("case", name, "chunk", chunk, flush=True)
     w, m = _model(s)
-    ids = _ids(s, 13)                                   # chunks of 8 + 5
+    m.set_prefill_chunk(chunk)
+    ids = _ids(s, 13)                                   # chunks of 8 + 5, or one of 13
     o = orc.Oracle(s, w, max_len=64)
     exact = [logits_ok(_np(m.prefill(ids)), o.prefill(ids), name + " prefill")[2]]
     tok = 7

@@ -66,11 +66,13 @@ def test_tiny_workload_generate_and_teacher_forced_logits(torch_cuda, orc):
     print("tiny: bitwise-equal logit fraction min %.4f mean %.4f" % (min(exact), np.mean(exact)))
 
 
+@pytest.mark.parametrize("chunk", [8, 16])
 @pytest.mark.parametrize("name", sorted(RAGGED))
-def test_ragged_shapes_teacher_forced(torch_cuda, orc, name):
+def test_ragged_shapes_teacher_forced(torch_cuda, orc, name, chunk):
     s = RAGGED[name]
     w, m = _model(s)
-    ids = _ids(s, 13)                                  # chunks of 8 + 5
+    m.set_prefill_chunk(chunk)
+    ids = _ids(s, 13)                                  # chunks of 8 + 5, or one of 13
     o = orc.Oracle(s, w, max_len=64)
     logits_ok(_np(m.prefill(ids)), o.prefill(ids), name + " prefill")
     tok = 7

@@ -38,6 +38,7 @@ def _model(shape, w, split_above, max_seq=512, max_batch=None):
     from transformer_forward_pass_amd import mak
     m = mak.MakModel(shape, w, max_seq=max_seq, max_batch=max_batch)
     m.set_attention_split(split_above)
+    m.set_prefill_chunk(8)     # per-column split-KV (16-token prompt steps run blockwise)
     return m
 
 

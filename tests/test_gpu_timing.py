@@ -75,16 +75,20 @@ def test_launches_per_decode_step_and_positive_times(split):
     m.free()
 
 
-def test_prefill_chunk_launches():
-    """A 13-token prompt in chunks of 8: two steps (8 + 5 tokens); the LM head
-    runs once, for the last token."""
+@pytest.mark.parametrize("chunk,steps", [(8, 2), (16, 1), (None, 1)])
+def test_prefill_chunk_launches(chunk, steps):
+    """A 13-token prompt in chunks of 8 takes two steps (8 + 5 tokens); in
+    chunks of 16, the default, one step of 13.  The LM head runs once, for
+    the last token."""
     m = _model()
+    if chunk:
+        m.set_prefill_chunk(chunk)
     L = SHAPE.n_layers
     m.set_phase_timing(True)
     m.prefill(_ids(13))
     t = m.phase_times()
     m.set_phase_timing(False)
     n = {k: v[1] for k, v in t.items()}
-    assert n == {"qkv": 2 * L, "attn": 2 * L, "o": 2 * L, "gateup": 2 * L, "down": 2 * L,
-                 "lmhead": 1, "ctl": 2}, n
+    assert n == {"qkv": steps * L, "attn": steps * L, "o": steps * L, "gateup": steps * L,
+                 "down": steps * L, "lmhead": 1, "ctl": steps}, n
     m.free()

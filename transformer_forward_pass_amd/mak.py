@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmak.so")
 
 MAK_OK, MAK_EINVAL, MAK_ERANGE, MAK_ENOMEM, MAK_EDEVICE = 0, -1, -2, -3, -4
 MAK_MAX_BATCH = 16
-MAK_PREFILL_CHUNK = 8
+MAK_PREFILL_CHUNK = 16
 
 EXPORTS = ("mak_quantize_mxfp4", "mak_plan", "mak_load", "mak_prefill", "mak_decode_step", "mak_decode_step_static", "mak_generate",
            "mak_decode_batch", "mak_batch_max", "mak_slot_length", "mak_read_kv", "mak_set_executor",

@@ -110,8 +110,9 @@ SHAPES: Dict[str, ModelShape] = {
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload(SHAPES["tiny"], prompt_len=16, max_new=32),
-    "smollm2-135m": Workload(SHAPES["smollm2-135m"], prompt_len=32, max_new=128),
-    "llama-3.2-1b": Workload(SHAPES["llama-3.2-1b"], prompt_len=32, max_new=128),
+    # the 32 + 128 batch-1 workloads: the prompt in two chunks of 16
+    "smollm2-135m": Workload(SHAPES["smollm2-135m"], prompt_len=32, max_new=128, chunk=16),
+    "llama-3.2-1b": Workload(SHAPES["llama-3.2-1b"], prompt_len=32, max_new=128, chunk=16),
     "qwen3-0.6b": Workload(SHAPES["qwen3-0.6b"], prompt_len=512, max_new=256),
     "tinyllama-1.1b": Workload(SHAPES["tinyllama-1.1b"], prompt_len=16, max_new=128,
                                batch=8, prompt_len_hi=256),
@@ -122,7 +123,8 @@ WORKLOADS: Dict[str, Workload] = {
     "llama-3.2-1b-p2040": Workload(SHAPES["llama-3.2-1b"], prompt_len=2040, max_new=4, chunk=16),
     # 4-bit (MXFP4) per-layer weights quantized from the same bf16 weights
     "llama-3.2-1b-mxfp4": Workload(dataclasses.replace(SHAPES["llama-3.2-1b"], name="llama-3.2-1b-mxfp4",
-                                                       weight_format="mxfp4"), prompt_len=32, max_new=128),
+                                                       weight_format="mxfp4"), prompt_len=32, max_new=128,
+                                 chunk=16),
 }
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
