@@ -51,7 +51,11 @@ constexpr int kAttnBlock = kAttnWaves * 64;
 //
 // LDS (dynamic): pv[4 * kAttnWaves][d] f64 | qf[d] f32 | kin[8][d] bf16 | vin[8][d] bf16 |
 //                rope cos, sin [9][d/2] bf16 | S[max_seq] f32
-template <int D_>
+// XM (Hq a multiple of 8 only): workgroups go to the 8 XCDs round-robin
+// (blockIdx % 8), so XCD x takes the query heads x*Hq/8 .. x*Hq/8 + Hq/8 - 1,
+// consecutive heads that share kv heads, and each XCD's L2 fetches the K/V
+// rows of as few kv heads as possible.
+template <int D_, bool XM = false>
 __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -59,7 +63,8 @@ __global__ __launch_bounds__(kAttnBlock) void k_attn(AttnPhase p)
     const int Hq = p.n_q_heads, Hkv = p.n_kv_heads, half = d >> 1;
     const int rep = Hq / Hkv;
     const int col = blockIdx.x / Hq;
-    const int h = blockIdx.x - col * Hq;
+    const int hr = blockIdx.x - col * Hq;
+    const int h = XM ? (hr & 7) * (Hq >> 3) + (hr >> 3) : hr;
     const int g = h / rep;
     const bool owner = (h - g * rep) == 0;        // appends the group's k', v
     const int q_dim = Hq * d, kv_dim = Hkv * d;
@@ -848,9 +853,11 @@ size_t mak_attn_lds(const AttnPhase& p)
 
 hipError_t mak_launch_attn(const AttnPhase& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1)
 {
-    const void* fn = reinterpret_cast<const void*>(&k_attn<0>);
-#define X(D) \
-    if (p.head_dim == D) fn = reinterpret_cast<const void*>(&k_attn<D>);
+    const bool xm = p.n_q_heads % 8 == 0;
+    const void* fn = xm ? reinterpret_cast<const void*>(&k_attn<0, true>) : reinterpret_cast<const void*>(&k_attn<0>);
+#define X(D)                                                                                \
+    if (p.head_dim == D)                                                                    \
+        fn = xm ? reinterpret_cast<const void*>(&k_attn<D, true>) : reinterpret_cast<const void*>(&k_attn<D>);
     MAK_ATTN_DIMS(X)
 #undef X
     AttnPhase q = p;
@@ -908,14 +915,13 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
         if (e != hipSuccess) return e;
     }
 #define X(D)                                                                               \
-    {                                                                                      \
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<D>),       \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,     \
+    for (const void* f : {reinterpret_cast<const void*>(&k_attn<D>),                       \
+                          reinterpret_cast<const void*>(&k_attn<D, true>)}) {              \
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,  \
                                            attn_bytes);                                    \
         if (e != hipSuccess) return e;                                                     \
     }
-    MAK_ATTN_DIMS(X)
+    MAK_ATTN_DIMS(X) X(0)
 #undef X
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<0>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, attn_bytes);
+    return hipSuccess;
 }
