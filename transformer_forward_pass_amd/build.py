@@ -56,7 +56,7 @@ MICRO_BIN = os.path.join(MICRO, "bin")
 
 
 def build_microbench(verbose: bool = False) -> None:
-    """Standalone measurement programs (sync_cost, mem_stream, copy_calib, bf16_convert)."""
+    """Standalone measurement programs (sync_cost, mem_stream, copy_calib, bf16_convert, fp64_mfma)."""
     os.makedirs(MICRO_BIN, exist_ok=True)
     srcs = sorted(f for f in os.listdir(MICRO) if f.endswith(".hip"))
 

@@ -66,6 +66,88 @@ __device__ __forceinline__ void chunk_f64(const uint4 v, double (&d)[8])
     d[7] = bf_hi(v.w);
 }
 
+// RMSNorm inputs of up to 16 columns into LDS as [chunk][column]
+// (kG16Slots slots per chunk, the last holding the norm weight's chunk):
+// wave w normalises columns w, w + NWAVES, ..., one at a time; lane chunks
+// lane + 64*i.  Inactive columns are stored as zeros.  Global loads already
+// in flight (a weight batch) stay in flight: the barriers fence LDS only.
+template <int NWAVES>
+__device__ __forceinline__ void gemm_stage_inputs(const GemvPhase& p, uint4* hsT, int lane, int wave)
+{
+    const int K = p.geo.k, C = K >> 3;
+    constexpr int SI = 8;                               // chunks per lane (K <= 4096)
+    const int n_i = (C + 63) >> 6;
+    const bool gather = p.in_kind == IN_GATHER_NORM;
+    const uint4* nw = reinterpret_cast<const uint4*>(p.norm_w);
+    // the norm weight is loaded once per workgroup (thread i: chunk i)
+    // into the pad slot of each staged chunk; every wave then reads it
+    // from LDS instead of loading all K of it for each of its columns
+    const bool w_ld = (int)threadIdx.x < C;
+    const uint4 wv = w_ld ? nw[threadIdx.x] : make_uint4(0, 0, 0, 0);
+    uint4 sv[16 / NWAVES][SI];
+    double ss[16 / NWAVES];
+#pragma unroll
+    for (int h = 0; h < 16 / NWAVES; h++) {
+        const int cw = wave + NWAVES * h;
+        const int col = p.col0 + min(cw, p.ncols - 1);
+        const uint4* base = gather ? reinterpret_cast<const uint4*>(p.embed)
+                                   : reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
+        const int token = gather ? p.ctl->cols[col].token : 0;
+#pragma unroll
+        for (int i = 0; i < SI; i++) {
+            if (i < n_i) {
+                const int q = min(lane + 64 * i, C - 1);
+                sv[h][i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
+            }
+        }
+    }
+    if (w_ld) hsT[threadIdx.x * kG16Slots + 16] = wv;
+#pragma unroll
+    for (int h = 0; h < 16 / NWAVES; h++) {
+        double a2 = 0.0;
+#pragma unroll
+        for (int i = 0; i < SI; i++) {
+            if (i < n_i && lane + 64 * i < C) {
+                const uint32_t u[4] = {sv[h][i].x, sv[h][i].y, sv[h][i].z, sv[h][i].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const double x0 = bf_lo(u[e]), x1 = bf_hi(u[e]);
+                    a2 = fma(x0, x0, a2);
+                    a2 = fma(x1, x1, a2);
+                }
+            }
+        }
+        ss[h] = wave_sum(a2);
+    }
+    lds_barrier();   // the norm weight in LDS (the weight batch stays in flight)
+#pragma unroll
+    for (int h = 0; h < 16 / NWAVES; h++) {
+        const int cw = wave + NWAVES * h;
+        const bool active = cw < p.ncols;
+        const float rs = rms_scale(ss[h], K, p.eps);
+        const bool store_x = active && p.in_kind == IN_GATHER_NORM && blockIdx.x == 0;
+        uint4* xs = reinterpret_cast<uint4*>(p.x_store + (size_t)(p.col0 + cw) * p.x_ld);
+#pragma unroll
+        for (int i = 0; i < SI; i++) {
+            const int q = lane + 64 * i;
+            if (i < n_i && q < C) {
+                if (store_x) xs[q] = sv[h][i];
+                const uint4 sw = hsT[q * kG16Slots + 16];
+                const uint32_t u[4] = {sv[h][i].x, sv[h][i].y, sv[h][i].z, sv[h][i].w};
+                const uint32_t ww[4] = {sw.x, sw.y, sw.z, sw.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    o[e] = rms_apply2(u[e], rs, ww[e]);
+                }
+                hsT[q * kG16Slots + cw] =
+                    active ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+    lds_barrier();   // (LDS only: the weight batch stays in flight)
+}
+
 template <int RT, int EPI, bool STAGED>
 __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) void k_gemm16(GemvPhase p)
 {
@@ -150,82 +232,10 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) voi
     // 1. the first weight batch, then the input staging (RMSNorm inputs):
     //    wave w normalises columns w, w + waves, ..., one at a time; lane
     //    chunks lane + 64*i.  The weights stay in flight throughout.
-    constexpr int SI = 8;                               // chunks per lane (K <= 4096)
-    const int n_i = (C + 63) >> 6;
     int grp_idx = blockIdx.x;
     set_rows(grp_idx);
     if (NB > 0) issue(bufA, 0);
-    if constexpr (STAGED) {
-        const bool gather = p.in_kind == IN_GATHER_NORM;
-        const uint4* nw = reinterpret_cast<const uint4*>(p.norm_w);
-        // the norm weight is loaded once per workgroup (thread i: chunk i)
-        // into the pad slot of each staged chunk; every wave then reads it
-        // from LDS instead of loading all K of it for each of its columns
-        const bool w_ld = (int)threadIdx.x < C;
-        const uint4 wv = w_ld ? nw[threadIdx.x] : make_uint4(0, 0, 0, 0);
-        uint4 sv[16 / kG16Waves][SI];
-        double ss[16 / kG16Waves];
-#pragma unroll
-        for (int h = 0; h < 16 / kG16Waves; h++) {
-            const int cw = wave + kG16Waves * h;
-            const int col = p.col0 + min(cw, p.ncols - 1);
-            const uint4* base = gather ? reinterpret_cast<const uint4*>(p.embed)
-                                       : reinterpret_cast<const uint4*>(p.in + (size_t)col * p.in_ld);
-            const int token = gather ? p.ctl->cols[col].token : 0;
-#pragma unroll
-            for (int i = 0; i < SI; i++) {
-                if (i < n_i) {
-                    const int q = min(lane + 64 * i, C - 1);
-                    sv[h][i] = base[gather ? packed_chunk(p.embed_geo, token, q) : (int64_t)q];
-                }
-            }
-        }
-        if (w_ld) hsT[threadIdx.x * kG16Slots + 16] = wv;
-#pragma unroll
-        for (int h = 0; h < 16 / kG16Waves; h++) {
-            double a2 = 0.0;
-#pragma unroll
-            for (int i = 0; i < SI; i++) {
-                if (i < n_i && lane + 64 * i < C) {
-                    const uint32_t u[4] = {sv[h][i].x, sv[h][i].y, sv[h][i].z, sv[h][i].w};
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const double x0 = bf_lo(u[e]), x1 = bf_hi(u[e]);
-                        a2 = fma(x0, x0, a2);
-                        a2 = fma(x1, x1, a2);
-                    }
-                }
-            }
-            ss[h] = wave_sum(a2);
-        }
-        lds_barrier();   // the norm weight in LDS (the weight batch stays in flight)
-#pragma unroll
-        for (int h = 0; h < 16 / kG16Waves; h++) {
-            const int cw = wave + kG16Waves * h;
-            const bool active = cw < p.ncols;
-            const float rs = rms_scale(ss[h], K, p.eps);
-            const bool store_x = active && p.in_kind == IN_GATHER_NORM && blockIdx.x == 0;
-            uint4* xs = reinterpret_cast<uint4*>(p.x_store + (size_t)(p.col0 + cw) * p.x_ld);
-#pragma unroll
-            for (int i = 0; i < SI; i++) {
-                const int q = lane + 64 * i;
-                if (i < n_i && q < C) {
-                    if (store_x) xs[q] = sv[h][i];
-                    const uint4 sw = hsT[q * kG16Slots + 16];
-                    const uint32_t u[4] = {sv[h][i].x, sv[h][i].y, sv[h][i].z, sv[h][i].w};
-                    const uint32_t ww[4] = {sw.x, sw.y, sw.z, sw.w};
-                    uint32_t o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        o[e] = rms_apply2(u[e], rs, ww[e]);
-                    }
-                    hsT[q * kG16Slots + cw] =
-                        active ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
-                }
-            }
-        }
-        lds_barrier();   // (LDS only: the weight batch stays in flight)
-    }
+    if constexpr (STAGED) gemm_stage_inputs<kG16Waves>(p, hsT, lane, wave);
 
     float best_v = -INFINITY;
     int best_i = 0x7fffffff;
@@ -362,6 +372,249 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) voi
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// k_gemm8: 2..8 columns on v_mfma_f64_4x4x4_4b_f64 (four independent 4x4x4
+// products per instruction), so no half of the matrix tile is padding.
+// Lane l (k-group kg = l / 16, block bq = (l / 4) % 4, e = l % 4) supplies
+// element t of the 16-byte chunk 4*blk + kg of tile row l % 16 as A (row e
+// of block bq) and of input column e (+4) as B; its result register is row
+// kg of block bq, column e (measured on the device), i.e. tile row
+// 4*bq + kg.  Two instructions per step share A: columns 0..3 and 4..7.
+// Work split, staging, K split over waves, the reduction in wave order and
+// the epilogues are those of k_gemm16.  Gate/up row pairs (2m, 2m + 1) sit
+// in lanes l and l ^ 16.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline size_t gemm8_part_lds(int rt, bool staged)
+{
+    return (size_t)gemm16_waves(rt, staged) * rt * 2 * 64 * 8;
+}
+
+template <int RT, int EPI, bool STAGED>
+__global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) ? 4 : 2) void k_gemm8(GemvPhase p)
+{
+    constexpr int kW = gemm16_waves(RT, STAGED);
+    constexpr int QB = 2;                   // 32-input blocks per batch
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ float bval[kW][8];
+    __shared__ int bidx[kW][8];
+    __shared__ int is_last;
+
+    const int K = p.geo.k, C = K >> 3;
+    const int KB = (C + 3) >> 2;                       // 32-input blocks
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = lane >> 4;                          // k-group (A, B) / result row in block
+    const int ti = lane & 15;                          // tile row loaded (A)
+    const int bq = (lane >> 2) & 3, e = lane & 3;      // block, column (B, result)
+    uint4* hsT = reinterpret_cast<uint4*>(smem);
+
+    const int kb0 = (int)((int64_t)wave * KB / kW);
+    const int kb1 = (int)((int64_t)(wave + 1) * KB / kW);
+    const int nkb = kb1 - kb0;
+    const int NB = (nkb + QB - 1) / QB;
+
+    const int lrl = p.geo.lr_log2, lr = 1 << lrl;
+    const int G = 64 >> lrl, R = p.geo.r;
+    const int rl = (R == 4) ? 2 : (R == 2) ? 1 : 0;
+    const int gl = 6 - lrl;
+    const int J = C >> lrl;
+    const int n_pad = p.geo.n_tiles * G * R;
+    const int N = p.geo.n_rows;
+    const uint4* W = reinterpret_cast<const uint4*>(p.w);
+    const int n_groups = (N + 16 * RT - 1) / (16 * RT);
+    const int rounds = (n_groups + (int)gridDim.x - 1) / (int)gridDim.x;
+    const bool alias = rounds == 1;
+    double* part = reinterpret_cast<double*>(smem + (STAGED && !alias ? gemm16_input_lds(K) : 0));
+
+    int64_t rbase[RT];
+    auto set_rows = [&](int grp_idx) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) {
+            int row = (grp_idx * RT + rt) * 16 + ti;
+            if (row >= n_pad) row = 0;                   // (padding beyond the matrix: result unused)
+            const int tile = row >> (gl + rl);
+            const int rr = row & ((G * R) - 1);
+            const int grp = rr >> rl, ri = rr & (R - 1);
+            rbase[rt] = ((int64_t)tile * J * R + ri) * 64 + grp * lr;
+        }
+    };
+    auto a_addr = [&](int rt, int c) __attribute__((always_inline)) {
+        const int j = c >> lrl, s = c & (lr - 1);
+        return rbase[rt] + (int64_t)j * R * 64 + s;
+    };
+    // raw inputs: this lane's two columns e and e + 4
+    const bool col_ok0 = e < p.ncols, col_ok1 = e + 4 < p.ncols;
+    const uint4* xin0 = reinterpret_cast<const uint4*>(p.in + (size_t)(p.col0 + min(e, p.ncols - 1)) * p.in_ld);
+    const uint4* xin1 = reinterpret_cast<const uint4*>(p.in + (size_t)(p.col0 + min(e + 4, p.ncols - 1)) * p.in_ld);
+
+    // one batch: per block q, RT weight chunks, then (raw inputs) the two
+    // input chunks, at [q * (RT + 2) + rt] and [q * (RT + 2) + RT + h]
+    constexpr int QL = QB * (RT + 2);
+    uint4 bufA[QL], bufB[QL];
+    auto issue = [&](uint4 (&buf)[QL], int bt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < QB; q++) {
+            const int kb = kb0 + min(bt * QB + q, max(nkb - 1, 0));
+            const int c = min(4 * kb + kg, C - 1);
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++) buf[q * (RT + 2) + rt] = ld_stream16(&W[a_addr(rt, c)]);
+            if constexpr (STAGED) {
+                buf[q * (RT + 2) + RT] = make_uint4(0, 0, 0, 0);
+                buf[q * (RT + 2) + RT + 1] = make_uint4(0, 0, 0, 0);
+            } else {
+                buf[q * (RT + 2) + RT] = xin0[c];
+                buf[q * (RT + 2) + RT + 1] = xin1[c];
+            }
+        }
+    };
+
+    int grp_idx = blockIdx.x;
+    set_rows(grp_idx);
+    if (NB > 0) issue(bufA, 0);
+    if constexpr (STAGED) gemm_stage_inputs<kW>(p, hsT, lane, wave);
+
+    float best_v[2] = {-INFINITY, -INFINITY};
+    int best_i[2] = {0x7fffffff, 0x7fffffff};
+
+    // one batch: QB blocks x RT tiles x 8 steps x 2 column halves; the
+    // steps rotate over CH accumulators per (tile, half)
+    constexpr int CH = 4 / RT > 1 ? 4 / RT : 1;
+    double acc[RT][2][CH];
+    auto compute = [&](const uint4 (&buf)[QL], int bt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < QB; q++) {
+            if (bt * QB + q >= nkb) break;               // wave-uniform
+            const int kb = kb0 + bt * QB + q;
+            const int c = 4 * kb + kg;
+            const bool in_k = c < C;
+            uint4 bv[2];
+            if constexpr (STAGED) {
+                bv[0] = hsT[min(c, C - 1) * kG16Slots + e];
+                bv[1] = hsT[min(c, C - 1) * kG16Slots + e + 4];
+            } else {
+                bv[0] = buf[q * (RT + 2) + RT];
+                bv[1] = buf[q * (RT + 2) + RT + 1];
+            }
+            const bool live0 = in_k && (STAGED || col_ok0), live1 = in_k && (STAGED || col_ok1);
+            bv[0] = make_uint4(live0 ? bv[0].x : 0u, live0 ? bv[0].y : 0u, live0 ? bv[0].z : 0u, live0 ? bv[0].w : 0u);
+            bv[1] = make_uint4(live1 ? bv[1].x : 0u, live1 ? bv[1].y : 0u, live1 ? bv[1].z : 0u, live1 ? bv[1].w : 0u);
+            double bd[2][8], ad[RT][8];
+            chunk_f64(bv[0], bd[0]);
+            chunk_f64(bv[1], bd[1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++) {
+                const uint4 av = buf[q * (RT + 2) + rt];
+                chunk_f64(make_uint4(in_k ? av.x : 0u, in_k ? av.y : 0u, in_k ? av.z : 0u, in_k ? av.w : 0u), ad[rt]);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; t++)
+#pragma unroll
+                for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+                        acc[rt][h][t % CH] = __builtin_amdgcn_mfma_f64_4x4x4f64(ad[rt][t], bd[h][t], acc[rt][h][t % CH], 0, 0, 0);
+        }
+    };
+
+    for (int round = 0; round < rounds; round++) {
+        const bool have = grp_idx < n_groups;
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int ch = 0; ch < CH; ch++) acc[rt][h][ch] = 0.0;
+        for (int bt = 0; bt < NB; bt += 2) {
+            batch_ready<QL>(bufA, QL);
+            if (bt + 1 < NB) issue(bufB, bt + 1);
+            compute(bufA, bt);
+            if (bt + 1 >= NB) break;
+            batch_ready<QL>(bufB, QL);
+            if (bt + 2 < NB) issue(bufA, bt + 2);
+            compute(bufB, bt + 1);
+        }
+        const int next_grp = grp_idx + (int)gridDim.x;
+        if (round + 1 < rounds) {
+            set_rows(min(next_grp, n_groups - 1));
+            if (NB > 0) issue(bufA, 0);
+        }
+        // partial tiles of the waves summed in wave order by wave rt
+        if (STAGED && alias) lds_barrier();              // every wave is done reading the inputs
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                double v = acc[rt][h][0];
+#pragma unroll
+                for (int ch = 1; ch < CH; ch++) v += acc[rt][h][ch];
+                part[((size_t)(wave * RT + rt) * 2 + h) * 64 + lane] = v;
+            }
+        lds_barrier();
+        if (wave < RT && have) {
+            const int rt = wave;
+            double y[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                double s = 0.0;
+#pragma unroll 4
+                for (int w2 = 0; w2 < kW; w2++) s += part[((size_t)(w2 * RT + rt) * 2 + h) * 64 + lane];
+                y[h] = s;
+            }
+            const int row = (grp_idx * RT + rt) * 16 + 4 * bq + kg;
+            if (EPI == EPI_SWIGLU) {
+                // rows 2m (gate, even kg) and 2m + 1 (up, lane ^ 16)
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const double yu = __shfl_xor(y[h], 16, 64);
+                    const int c = e + 4 * h;
+                    if (!(kg & 1) && c < p.ncols && row + 1 < N) {
+                        const float gv = rbf((float)y[h]);
+                        const float uv = rbf((float)yu);
+                        const double gd = (double)gv;
+                        const float z = rbf((float)(gd / (1.0 + exp(-gd))));
+                        p.out[(size_t)(p.col0 + c) * p.out_ld + (row >> 1)] = f2bf(z * uv);
+                    }
+                }
+            } else if (row < N) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int c = e + 4 * h;
+                    if (c >= p.ncols) continue;
+                    const size_t col = (size_t)(p.col0 + c);
+                    if (EPI == EPI_STORE) {
+                        p.out[col * p.out_ld + row] = f2bf((float)y[h]);
+                    } else if (EPI == EPI_RESIDUAL) {
+                        const float xr = bf2f(p.out[col * p.out_ld + row]);
+                        p.out[col * p.out_ld + row] = f2bf(xr + rbf((float)y[h]));
+                    } else {   // EPI_LOGITS
+                        const float v = (float)y[h];
+                        p.logits[(size_t)c * p.logits_ld + row] = v;
+                        if (v > best_v[h] || (v == best_v[h] && row < best_i[h])) {
+                            best_v[h] = v;
+                            best_i[h] = row;
+                        }
+                    }
+                }
+            }
+        }
+        lds_barrier();   // `part` is rewritten by the next round
+        grp_idx = next_grp;
+    }
+
+    if (EPI == EPI_LOGITS) {
+        // per-lane bests belong to columns e and e + 4
+        float bv[8];
+        int bi[8];
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            bv[c] = (c == e) ? best_v[0] : (c == e + 4) ? best_v[1] : -INFINITY;
+            bi[c] = (c == e) ? best_i[0] : (c == e + 4) ? best_i[1] : 0x7fffffff;
+        }
+        argmax_tail<8>(p, bv, bi, bval, bidx, is_last, lane, wave, kW);
+    }
+}
+
 }  // namespace mak
 
 using namespace mak;
@@ -400,3 +653,32 @@ size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round)
 
 // workgroup size of k_gemm16 with rt row tiles (staged: RMSNorm inputs)
 int mak_gemm16_threads(int rt, bool staged) { return gemm16_waves(rt, staged) * 64; }
+
+const void* mak_gemm8_fn(int rt, int epi, bool staged)
+{
+#define X(RT, S)                                                                                         \
+    if (rt == RT && staged == S) {                                                                       \
+        switch (epi) {                                                                                   \
+        case EPI_STORE: return reinterpret_cast<const void*>(&k_gemm8<RT, EPI_STORE, S>);                \
+        case EPI_RESIDUAL: return reinterpret_cast<const void*>(&k_gemm8<RT, EPI_RESIDUAL, S>);          \
+        case EPI_SWIGLU: return reinterpret_cast<const void*>(&k_gemm8<RT, EPI_SWIGLU, S>);              \
+        case EPI_LOGITS: return reinterpret_cast<const void*>(&k_gemm8<RT, EPI_LOGITS, S>);              \
+        }                                                                                                \
+    }
+    X(1, true)
+    X(2, true)
+    X(4, true)
+    X(1, false)
+    X(2, false)
+#undef X
+    return nullptr;   // (raw inputs take at most two row tiles: mak_gemm8_plan)
+}
+
+// dynamic LDS of a k_gemm8 launch (single_round: the partial tiles reuse the
+// staged inputs' space)
+size_t mak_gemm8_lds(int rt, int k, bool staged, bool single_round)
+{
+    if (!staged) return gemm8_part_lds(rt, false);
+    return single_round ? std::max(gemm16_input_lds(k), gemm8_part_lds(rt, true))
+                        : gemm16_input_lds(k) + gemm8_part_lds(rt, true);
+}

@@ -38,6 +38,7 @@ int mak_gemv_nc(int ncols);
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n);
 size_t mak_gemv_lds(const GemvPhase& p);
 int mak_gemm16_plan(const GemvPhase& p, int ncols, size_t lds_budget);
+int mak_gemm8_plan(const GemvPhase& p, int ncols, size_t lds_budget);
 int mak_check_launch(const void* fn, dim3 grid, dim3 block, size_t lds);
 const char* mak_launch_check_msg();
 
@@ -559,7 +560,7 @@ int run_gemv(mak_model* m, int kind, GemvPhase p, int ncols, int col0)
     // kernel stages at most 16 RMSNorm inputs of K <= 4096 and reads raw
     // inputs from memory: one launch)
     const bool q4 = p.geo.fmt == MAK_FMT_MXFP4;
-    const bool mfma = !q4 && mak_gemm16_plan(p, ncols, kLdsBudgetN) != 0;
+    const bool mfma = !q4 && (mak_gemm16_plan(p, ncols, kLdsBudgetN) != 0 || mak_gemm8_plan(p, ncols, kLdsBudgetN) != 0);
     const int step = q4 ? max_cols_for_k4(p.geo.k)
                         : (p.epi == EPI_LOGITS || mfma) ? ncols : max_cols_for_k(p.geo.k);
     if (q4 && p.epi == EPI_LOGITS) return fail(MAK_EINVAL, "internal: 4-bit LM head");
