@@ -90,6 +90,21 @@ def _gemv_bytes(shape, kind):
     return None
 
 
+def _on_matrix_cores(shape, kind, ncols):
+    """Whether the library's planner runs a multi-column GEMM of this kind on
+    the fp64 matrix cores: 9-16 columns always (k_gemm16); 2-8 columns where
+    it picks k_gemm8 (at least 2048 inputs and 2048 rows, raw inputs -- O and
+    down -- only at 2048 inputs)."""
+    if ncols >= 9:
+        return True
+    if ncols < 2:
+        return False
+    H, I = shape.hidden, shape.intermediate
+    n, k, staged = {"qkv": (shape.q_dim + 2 * shape.kv_dim, H, True), "o": (H, shape.q_dim, False),
+                    "gateup": (2 * I, H, True), "down": (H, I, False), "lmhead": (shape.vocab, H, True)}[kind]
+    return k >= 2048 and n >= 2048 and (staged or k == 2048)
+
+
 def _attn_bytes(shape, p0, n_new, chunk=8):
     """Algorithmic bytes of the attention launches of one generate call
     (prompt of p0 tokens in chunks, then n_new - 1 decode steps), and their
@@ -308,8 +323,8 @@ def measure_batched(args, name="tinyllama-1.1b", reps=2):
                               "achieved_gbs": round(step_bytes / t_step / 1e9, 2),
                               "frac": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4)},
             # fp64 rate of the dominant GEMM: 2 flops per weight per sequence
-            # (16-column groups run on the fp64 matrix cores, 8 on the VALU)
-            "mfma_roofline": {"bound": "mfma" if B >= 9 else "alu", "kernel": dom,
+            # (on the fp64 matrix cores or on the vector units, as planned)
+            "mfma_roofline": {"bound": "mfma" if _on_matrix_cores(shape, dom, B) else "alu", "kernel": dom,
                               "achieved": round(per_launch / 2 * 2 * B / avg_s / 1e12, 3),
                               "peak": FP64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s (fp64)",
                               "frac": round(per_launch * B / avg_s / 1e12 / FP64_MFMA_PEAK_TFLOPS, 4)},
