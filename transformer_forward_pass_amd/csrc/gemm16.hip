@@ -390,7 +390,11 @@ __host__ __device__ inline size_t gemm8_part_lds(int rt, bool staged)
     return (size_t)gemm16_waves(rt, staged) * rt * 2 * 64 * 8;
 }
 
-template <int RT, int EPI, bool STAGED>
+// HALF: tiles of 8 rows, twice the row groups of a short matrix.  Blocks
+// b and b + 2 take the same rows 4*(b % 2) .. +3 over two consecutive
+// 32-input blocks, and lanes l and l ^ 8 add their halves before the
+// cross-wave sum.
+template <int RT, int EPI, bool STAGED, bool HALF = false>
 __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) ? 4 : 2) void k_gemm8(GemvPhase p)
 {
     constexpr int kW = gemm16_waves(RT, STAGED);
@@ -405,14 +409,17 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kg = lane >> 4;                          // k-group (A, B) / result row in block
-    const int ti = lane & 15;                          // tile row loaded (A)
     const int bq = (lane >> 2) & 3, e = lane & 3;      // block, column (B, result)
+    constexpr int TR = HALF ? 8 : 16;                  // rows per tile
+    const int ti = HALF ? 4 * (bq & 1) + e : lane & 15;   // tile row loaded (A)
+    const int kh = HALF ? bq >> 1 : 0;                 // HALF: which block of a pair
     uint4* hsT = reinterpret_cast<uint4*>(smem);
 
     const int kb0 = (int)((int64_t)wave * KB / kW);
     const int kb1 = (int)((int64_t)(wave + 1) * KB / kW);
     const int nkb = kb1 - kb0;
-    const int NB = (nkb + QB - 1) / QB;
+    const int NU = HALF ? (nkb + 1) >> 1 : nkb;        // steps: blocks, or pairs of blocks
+    const int NB = (NU + QB - 1) / QB;
 
     const int lrl = p.geo.lr_log2, lr = 1 << lrl;
     const int G = 64 >> lrl, R = p.geo.r;
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     const int n_pad = p.geo.n_tiles * G * R;
     const int N = p.geo.n_rows;
     const uint4* W = reinterpret_cast<const uint4*>(p.w);
-    const int n_groups = (N + 16 * RT - 1) / (16 * RT);
+    const int n_groups = (N + TR * RT - 1) / (TR * RT);
     const int rounds = (n_groups + (int)gridDim.x - 1) / (int)gridDim.x;
     const bool alias = rounds == 1;
     double* part = reinterpret_cast<double*>(smem + (STAGED && !alias ? gemm16_input_lds(K) : 0));
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     auto set_rows = [&](int grp_idx) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < RT; rt++) {
-            int row = (grp_idx * RT + rt) * 16 + ti;
+            int row = (grp_idx * RT + rt) * TR + ti;
             if (row >= n_pad) row = 0;                   // (padding beyond the matrix: result unused)
             const int tile = row >> (gl + rl);
             const int rr = row & ((G * R) - 1);
@@ -455,7 +462,8 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     auto issue = [&](uint4 (&buf)[QL], int bt) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < QB; q++) {
-            const int kb = kb0 + min(bt * QB + q, max(nkb - 1, 0));
+            const int u = HALF ? 2 * (bt * QB + q) + kh : bt * QB + q;
+            const int kb = kb0 + min(u, max(nkb - 1, 0));
             const int c = min(4 * kb + kg, C - 1);
 #pragma unroll
             for (int rt = 0; rt < RT; rt++) buf[q * (RT + 2) + rt] = ld_stream16(&W[a_addr(rt, c)]);
@@ -484,10 +492,11 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     auto compute = [&](const uint4 (&buf)[QL], int bt) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < QB; q++) {
-            if (bt * QB + q >= nkb) break;               // wave-uniform
-            const int kb = kb0 + bt * QB + q;
+            if (bt * QB + q >= NU) break;                // wave-uniform
+            const int u = HALF ? 2 * (bt * QB + q) + kh : bt * QB + q;
+            const int kb = kb0 + u;
             const int c = 4 * kb + kg;
-            const bool in_k = c < C;
+            const bool in_k = c < C && u < nkb;
             uint4 bv[2];
             if constexpr (STAGED) {
                 bv[0] = hsT[min(c, C - 1) * kG16Slots + e];
@@ -548,10 +557,11 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
                 double v = acc[rt][h][0];
 #pragma unroll
                 for (int ch = 1; ch < CH; ch++) v += acc[rt][h][ch];
+                if (HALF) v += __shfl_xor(v, 8, 64);     // the other block of the pair
                 part[((size_t)(wave * RT + rt) * 2 + h) * 64 + lane] = v;
             }
         lds_barrier();
-        if (wave < RT && have) {
+        if (wave < RT && have && (!HALF || kh == 0 || EPI == EPI_SWIGLU)) {
             const int rt = wave;
             double y[2];
 #pragma unroll
@@ -561,14 +571,14 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
                 for (int w2 = 0; w2 < kW; w2++) s += part[((size_t)(w2 * RT + rt) * 2 + h) * 64 + lane];
                 y[h] = s;
             }
-            const int row = (grp_idx * RT + rt) * 16 + 4 * bq + kg;
+            const int row = (grp_idx * RT + rt) * TR + (HALF ? 4 * (bq & 1) : 4 * bq) + kg;
             if (EPI == EPI_SWIGLU) {
                 // rows 2m (gate, even kg) and 2m + 1 (up, lane ^ 16)
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const double yu = __shfl_xor(y[h], 16, 64);
                     const int c = e + 4 * h;
-                    if (!(kg & 1) && c < p.ncols && row + 1 < N) {
+                    if (!(kg & 1) && kh == 0 && c < p.ncols && row + 1 < N) {
                         const float gv = rbf((float)y[h]);
                         const float uv = rbf((float)yu);
                         const double gd = (double)gv;
@@ -654,8 +664,18 @@ size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round)
 // workgroup size of k_gemm16 with rt row tiles (staged: RMSNorm inputs)
 int mak_gemm16_threads(int rt, bool staged) { return gemm16_waves(rt, staged) * 64; }
 
-const void* mak_gemm8_fn(int rt, int epi, bool staged)
+const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half)
 {
+    if (half) {   // one tile of 8 rows, raw inputs
+        if (rt != 1 || staged) return nullptr;
+        switch (epi) {
+        case EPI_STORE: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_STORE, false, true>);
+        case EPI_RESIDUAL: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_RESIDUAL, false, true>);
+        case EPI_SWIGLU: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_SWIGLU, false, true>);
+        case EPI_LOGITS: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_LOGITS, false, true>);
+        }
+        return nullptr;
+    }
 #define X(RT, S)                                                                                         \
     if (rt == RT && staged == S) {                                                                       \
         switch (epi) {                                                                                   \

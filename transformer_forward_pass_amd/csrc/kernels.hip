@@ -362,7 +362,7 @@ static const void* gemv_fn_r1(int epi)
 
 // gemm16.hip: the multi-column GEMM on the fp64 matrix cores
 const void* mak_gemm16_fn(int rt, int epi, bool staged);
-const void* mak_gemm8_fn(int rt, int epi, bool staged);
+const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half);
 size_t mak_gemm8_lds(int rt, int k, bool staged, bool single_round);
 size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round);
 int mak_gemm16_threads(int rt, bool staged);
@@ -420,7 +420,7 @@ static const void* gemv_fn(const GemvPhase& p)
         return mak_gemv4_fn(p.geo.r, mak_gemv_nc(p.ncols), p.epi);
     }
     if (p.multi == 2) return mak_gemm16_fn(p.rr, p.epi, p.in_kind != IN_RAW);
-    if (p.multi == 3) return mak_gemm8_fn(p.rr, p.epi, p.in_kind != IN_RAW);
+    if (p.multi == 3) return mak_gemm8_fn(p.rr, p.epi, p.in_kind != IN_RAW, p.jw == 2);
     if (p.multi) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
     if (const void* f = gemv1_fn(p)) return f;
     switch (p.geo.r) {
@@ -437,7 +437,8 @@ size_t mak_gemv_lds(const GemvPhase& p)
 {
     if (p.geo.fmt == MAK_FMT_MXFP4) return mak_gemv4_lds(p.geo.k, mak_gemv_nc(p.ncols));
     if (p.multi == 2 || p.multi == 3) {
-        const int64_t groups = (p.geo.n_rows + 16 * p.rr - 1) / (16 * p.rr);
+        const int tr = (p.multi == 3 && p.jw == 2) ? 8 : 16;   // rows per tile (k_gemm8 half-height: jw = 2)
+        const int64_t groups = (p.geo.n_rows + tr * p.rr - 1) / (tr * p.rr);
         return p.multi == 2 ? mak_gemm16_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks)
                             : mak_gemm8_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks);
     }
@@ -647,7 +648,19 @@ int mak_gemm16_plan(const GemvPhase& p, int ncols, size_t lds_budget)
 // (shorter rows leave each wave too few 32-input blocks to cover the
 // staging and the cross-wave sum; long raw rows over few row groups leave
 // CUs idle).  Row tiles per workgroup as for k_gemm16, raw inputs at most
-// two.  Returns 0 if the kernel does not apply.
+// two.  Raw inputs whose 16-row groups are fewer than the CUs take tiles of
+// 8 rows (gemm8_half; MAK_GEMM8_HALF=0 turns them off), and with them any
+// K.  Returns 0 if the kernel does not apply.
+static bool gemm8_half(const GemvPhase& p)
+{
+    static int hv = -1;
+    if (hv < 0) {
+        const char* e = getenv("MAK_GEMM8_HALF");
+        hv = (e && atoi(e) == 0) ? 0 : 1;
+    }
+    return hv && p.in_kind == IN_RAW && (p.geo.n_rows + 15) / 16 < device_cus();
+}
+
 int mak_gemm8_plan(const GemvPhase& p, int ncols, size_t lds_budget)
 {
     static int mc = -1;
@@ -658,11 +671,13 @@ int mak_gemm8_plan(const GemvPhase& p, int ncols, size_t lds_budget)
     if (mc == 0 || ncols < mc || ncols < 2 || ncols > 8) return 0;
     const bool staged = p.in_kind != IN_RAW;
     if (staged && p.geo.k > 4096) return 0;
-    if (p.geo.k < 2048 || p.geo.n_rows < 2048 || (!staged && p.geo.k > 2048)) return 0;
+    const bool half = gemm8_half(p);
+    if (p.geo.k < 2048 || p.geo.n_rows < 2048 || (!staged && p.geo.k > 2048 && !half)) return 0;
     const int n_cu = device_cus();
     const int n16 = (p.geo.n_rows + 15) / 16;
     int rt = (n16 >= 8 * n_cu) ? 4 : (n16 >= 4 * n_cu) ? 2 : 1;
     if (!staged && rt > 2) rt = 2;
+    if (half) rt = 1;
     while (rt > 1 && mak_gemm8_lds(rt, p.geo.k, staged, false) > lds_budget) rt >>= 1;
     return mak_gemm8_lds(rt, p.geo.k, staged, false) <= lds_budget ? rt : 0;
 }
@@ -690,11 +705,13 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             // (as k_gemm16 below: resident workgroups, each staging its inputs once)
             p.multi = 3;
             p.rr = rt;
-            p.jw = 1;
+            const bool half = gemm8_half(p);
+            p.jw = half ? 2 : 1;                      // (k_gemm8: 2 = tiles of 8 rows)
             const bool staged = p.in_kind != IN_RAW;
             p.threads = mak_gemm16_threads(rt, staged);
-            const int64_t groups = (p.geo.n_rows + 16 * rt - 1) / (16 * rt);
-            const int occ = resident_blocks(mak_gemm8_fn(rt, p.epi, staged), p.threads,
+            const int tr = half ? 8 : 16;
+            const int64_t groups = (p.geo.n_rows + tr * rt - 1) / (tr * rt);
+            const int occ = resident_blocks(mak_gemm8_fn(rt, p.epi, staged, half), p.threads,
                                             mak_gemm8_lds(rt, p.geo.k, staged, false));
             int64_t g = std::min<int64_t>(groups, (int64_t)occ * n_cu);
             if (p.epi == EPI_LOGITS) g = std::min<int64_t>(g, cap);
@@ -944,10 +961,11 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
             for (bool staged : {true, false}) {
                 hipError_t e = set(mak_gemm16_fn(rt, epi, staged), bytes_n);
                 if (e != hipSuccess) return e;
-                if (const void* f8 = mak_gemm8_fn(rt, epi, staged)) {
-                    e = set(f8, bytes_n);
-                    if (e != hipSuccess) return e;
-                }
+                for (bool half : {false, true})
+                    if (const void* f8 = mak_gemm8_fn(rt, epi, staged, half)) {
+                        e = set(f8, bytes_n);
+                        if (e != hipSuccess) return e;
+                    }
             }
     for (int r : {1, 2, 4})
         for (int j : {1, 2, 3, 4, 6, 9, 11, 16})
