@@ -1,12 +1,15 @@
 """Steps of 2..8 columns on the fp64 matrix cores (v_mfma_f64_4x4x4_4b_f64,
 k_gemm8), which the planner picks for GEMMs of at least 2048 inputs and
-2048 rows (raw inputs only at 2048).  A one-layer shape inside that region
-runs every epilogue through it: QKV (RMSNorm inputs, store), O (raw inputs,
-residual), gate/up (RMSNorm inputs, SwiGLU), down (raw inputs, residual) and
-the LM head (RMSNorm inputs, logits and greedy argmax).  Batched decode must
-equal decoding each sequence alone (the one-column kernels) bitwise, a
-chunked prompt must equal token-by-token consumption bitwise, and both must
-match the CPU oracle ("model-as-a-kernel", API: decode_batch and chunked
+2048 rows, with tiles of 8 rows for raw inputs whose 16-row groups would be
+fewer than the CUs.  Two one-layer shapes inside that region run every
+epilogue through it: QKV (RMSNorm inputs, store), O (raw inputs, residual),
+gate/up (RMSNorm inputs, SwiGLU), down (raw inputs, residual) and the LM
+head (RMSNorm inputs, logits and greedy argmax); O and down on 8-row tiles,
+the rest on 16-row tiles (the second shape: a 3072-row gate/up and a
+6144-row LM head; its 1536-input down stays on the vector units).  Batched
+decode must equal decoding each sequence alone (the one-column kernels)
+bitwise, a chunked prompt must equal token-by-token consumption bitwise, and
+both must match the CPU oracle ("model-as-a-kernel", API: decode_batch and chunked
 prompt consumption; every dot product exact before its single rounding)."""
 import numpy as np
 import pytest
@@ -16,8 +19,12 @@ from transformer_forward_pass_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-SHAPE = synth.small_shape(n_layers=1, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
-                          intermediate=2048, vocab=2048, max_batch=8)
+SHAPES = {
+    "i2048": synth.small_shape(n_layers=1, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                               intermediate=2048, vocab=2048, max_batch=8),
+    "i1536": synth.small_shape(n_layers=1, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                               intermediate=1536, vocab=6144, max_batch=8),
+}
 STEPS = 3
 
 
@@ -28,28 +35,34 @@ def torch_cuda():
     return torch
 
 
-@pytest.fixture(scope="module")
-def weights():
-    return synth.make_weights(SHAPE)
+_W = {}
+
+
+def _weights(name):
+    if name not in _W:
+        _W[name] = synth.make_weights(SHAPES[name])
+    return _W[name]
 
 
 def _np(t):
     return t.double().cpu().numpy()
 
 
-def _prompts(n, seed=5):
+def _prompts(shape, n, seed=5):
     rng = np.random.default_rng(seed)
     lens = rng.integers(3, 17, n)
-    return [[int(t) for t in rng.integers(0, SHAPE.vocab, int(k))] for k in lens]
+    return [[int(t) for t in rng.integers(0, shape.vocab, int(k))] for k in lens]
 
 
 @pytest.mark.parametrize("B", [8, 5, 2])
-def test_batch_equals_alone_and_oracle(torch_cuda, orc, weights, B):
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_batch_equals_alone_and_oracle(torch_cuda, orc, name, B):
     """B sequences decoded together (full and partial column groups) equal
     each decoded alone, tokens and logits, and match the oracle."""
     from transformer_forward_pass_amd import mak
-    print("case B=%d" % B, flush=True)
-    prompts = _prompts(B)
+    print("case %s B=%d" % (name, B), flush=True)
+    SHAPE, weights = SHAPES[name], _weights(name)
+    prompts = _prompts(SHAPE, B)
     bat = mak.MakModel(SHAPE, weights, max_seq=64, max_batch=8)
     one = mak.MakModel(SHAPE, weights, max_seq=64, max_batch=8)
     for b, p in enumerate(prompts):
@@ -74,12 +87,15 @@ def test_batch_equals_alone_and_oracle(torch_cuda, orc, weights, B):
     one.free()
 
 
-def test_chunked_prompt_equals_token_by_token_and_oracle(torch_cuda, orc, weights):
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_chunked_prompt_equals_token_by_token_and_oracle(torch_cuda, orc, name):
     """A 13-token prompt in chunks of 8 (steps of 8 and 5 columns) equals
     consuming it one token at a time, logits and KV cache bitwise, and
     matches the oracle."""
     from transformer_forward_pass_amd import mak
-    ids = _prompts(1, seed=9)[0] + _prompts(1, seed=10)[0]
+    print("case %s chunked" % name, flush=True)
+    SHAPE, weights = SHAPES[name], _weights(name)
+    ids = _prompts(SHAPE, 1, seed=9)[0] + _prompts(SHAPE, 1, seed=10)[0]
     ids = (ids * 2)[:13]
     runs = []
     for chunk in (8, 1):
