@@ -385,23 +385,25 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, RT == 1 ? 4 : 2) voi
 // the epilogues are those of k_gemm16.  Gate/up row pairs (2m, 2m + 1) sit
 // in lanes l and l ^ 16.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline size_t gemm8_part_lds(int rt, bool staged)
+__host__ __device__ inline size_t gemm8_part_lds(int rt, bool staged, int ng)
 {
-    return (size_t)gemm16_waves(rt, staged) * rt * 2 * 64 * 8;
+    return (size_t)gemm16_waves(rt, staged) * rt * ng * 64 * 8;
 }
 
 // HALF: tiles of 8 rows, twice the row groups of a short matrix.  Blocks
 // b and b + 2 take the same rows 4*(b % 2) .. +3 over two consecutive
 // 32-input blocks, and lanes l and l ^ 8 add their halves before the
 // cross-wave sum.
-template <int RT, int EPI, bool STAGED, bool HALF = false>
+// NG: groups of 4 columns (2: up to 8 columns; 4: up to 16, raw inputs on
+// half-height tiles), each one instruction per step sharing A.
+template <int RT, int EPI, bool STAGED, bool HALF = false, int NG = 2>
 __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) ? 4 : 2) void k_gemm8(GemvPhase p)
 {
     constexpr int kW = gemm16_waves(RT, STAGED);
     constexpr int QB = 2;                   // 32-input blocks per batch
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ float bval[kW][8];
-    __shared__ int bidx[kW][8];
+    __shared__ float bval[kW][4 * NG];
+    __shared__ int bidx[kW][4 * NG];
     __shared__ int is_last;
 
     const int K = p.geo.k, C = K >> 3;
@@ -450,14 +452,18 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
         const int j = c >> lrl, s = c & (lr - 1);
         return rbase[rt] + (int64_t)j * R * 64 + s;
     };
-    // raw inputs: this lane's two columns e and e + 4
-    const bool col_ok0 = e < p.ncols, col_ok1 = e + 4 < p.ncols;
-    const uint4* xin0 = reinterpret_cast<const uint4*>(p.in + (size_t)(p.col0 + min(e, p.ncols - 1)) * p.in_ld);
-    const uint4* xin1 = reinterpret_cast<const uint4*>(p.in + (size_t)(p.col0 + min(e + 4, p.ncols - 1)) * p.in_ld);
+    // raw inputs: this lane's columns e, e + 4, ...
+    bool col_ok[NG];
+    const uint4* xin[NG];
+#pragma unroll
+    for (int h = 0; h < NG; h++) {
+        col_ok[h] = e + 4 * h < p.ncols;
+        xin[h] = reinterpret_cast<const uint4*>(p.in + (size_t)(p.col0 + min(e + 4 * h, p.ncols - 1)) * p.in_ld);
+    }
 
-    // one batch: per block q, RT weight chunks, then (raw inputs) the two
-    // input chunks, at [q * (RT + 2) + rt] and [q * (RT + 2) + RT + h]
-    constexpr int QL = QB * (RT + 2);
+    // one batch: per block q, RT weight chunks, then (raw inputs) the NG
+    // input chunks, at [q * (RT + NG) + rt] and [q * (RT + NG) + RT + h]
+    constexpr int QL = QB * (RT + NG);
     uint4 bufA[QL], bufB[QL];
     auto issue = [&](uint4 (&buf)[QL], int bt) __attribute__((always_inline)) {
 #pragma unroll
@@ -466,14 +472,10 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
             const int kb = kb0 + min(u, max(nkb - 1, 0));
             const int c = min(4 * kb + kg, C - 1);
 #pragma unroll
-            for (int rt = 0; rt < RT; rt++) buf[q * (RT + 2) + rt] = ld_stream16(&W[a_addr(rt, c)]);
-            if constexpr (STAGED) {
-                buf[q * (RT + 2) + RT] = make_uint4(0, 0, 0, 0);
-                buf[q * (RT + 2) + RT + 1] = make_uint4(0, 0, 0, 0);
-            } else {
-                buf[q * (RT + 2) + RT] = xin0[c];
-                buf[q * (RT + 2) + RT + 1] = xin1[c];
-            }
+            for (int rt = 0; rt < RT; rt++) buf[q * (RT + NG) + rt] = ld_stream16(&W[a_addr(rt, c)]);
+#pragma unroll
+            for (int h = 0; h < NG; h++)
+                buf[q * (RT + NG) + RT + h] = STAGED ? make_uint4(0, 0, 0, 0) : xin[h][c];
         }
     };
 
@@ -482,13 +484,18 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     if (NB > 0) issue(bufA, 0);
     if constexpr (STAGED) gemm_stage_inputs<kW>(p, hsT, lane, wave);
 
-    float best_v[2] = {-INFINITY, -INFINITY};
-    int best_i[2] = {0x7fffffff, 0x7fffffff};
+    float best_v[NG];
+    int best_i[NG];
+#pragma unroll
+    for (int h = 0; h < NG; h++) {
+        best_v[h] = -INFINITY;
+        best_i[h] = 0x7fffffff;
+    }
 
     // one batch: QB blocks x RT tiles x 8 steps x 2 column halves; the
     // steps rotate over CH accumulators per (tile, half)
-    constexpr int CH = 4 / RT > 1 ? 4 / RT : 1;
-    double acc[RT][2][CH];
+    constexpr int CH = 8 / (RT * NG) > 1 ? 8 / (RT * NG) : 1;
+    double acc[RT][NG][CH];
     auto compute = [&](const uint4 (&buf)[QL], int bt) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < QB; q++) {
@@ -497,23 +504,17 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
             const int kb = kb0 + u;
             const int c = 4 * kb + kg;
             const bool in_k = c < C && u < nkb;
-            uint4 bv[2];
-            if constexpr (STAGED) {
-                bv[0] = hsT[min(c, C - 1) * kG16Slots + e];
-                bv[1] = hsT[min(c, C - 1) * kG16Slots + e + 4];
-            } else {
-                bv[0] = buf[q * (RT + 2) + RT];
-                bv[1] = buf[q * (RT + 2) + RT + 1];
+            double bd[NG][8], ad[RT][8];
+#pragma unroll
+            for (int h = 0; h < NG; h++) {
+                uint4 bv = STAGED ? hsT[min(c, C - 1) * kG16Slots + e + 4 * h] : buf[q * (RT + NG) + RT + h];
+                const bool live = in_k && (STAGED || col_ok[h]);
+                bv = make_uint4(live ? bv.x : 0u, live ? bv.y : 0u, live ? bv.z : 0u, live ? bv.w : 0u);
+                chunk_f64(bv, bd[h]);
             }
-            const bool live0 = in_k && (STAGED || col_ok0), live1 = in_k && (STAGED || col_ok1);
-            bv[0] = make_uint4(live0 ? bv[0].x : 0u, live0 ? bv[0].y : 0u, live0 ? bv[0].z : 0u, live0 ? bv[0].w : 0u);
-            bv[1] = make_uint4(live1 ? bv[1].x : 0u, live1 ? bv[1].y : 0u, live1 ? bv[1].z : 0u, live1 ? bv[1].w : 0u);
-            double bd[2][8], ad[RT][8];
-            chunk_f64(bv[0], bd[0]);
-            chunk_f64(bv[1], bd[1]);
 #pragma unroll
             for (int rt = 0; rt < RT; rt++) {
-                const uint4 av = buf[q * (RT + 2) + rt];
+                const uint4 av = buf[q * (RT + NG) + rt];
                 chunk_f64(make_uint4(in_k ? av.x : 0u, in_k ? av.y : 0u, in_k ? av.z : 0u, in_k ? av.w : 0u), ad[rt]);
             }
 #pragma unroll
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
 #pragma unroll
                 for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-                    for (int h = 0; h < 2; h++)
+                    for (int h = 0; h < NG; h++)
                         acc[rt][h][t % CH] = __builtin_amdgcn_mfma_f64_4x4x4f64(ad[rt][t], bd[h][t], acc[rt][h][t % CH], 0, 0, 0);
         }
     };
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
 #pragma unroll
         for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-            for (int h = 0; h < 2; h++)
+            for (int h = 0; h < NG; h++)
 #pragma unroll
                 for (int ch = 0; ch < CH; ch++) acc[rt][h][ch] = 0.0;
         for (int bt = 0; bt < NB; bt += 2) {
@@ -553,29 +554,29 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
 #pragma unroll
         for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
+            for (int h = 0; h < NG; h++) {
                 double v = acc[rt][h][0];
 #pragma unroll
                 for (int ch = 1; ch < CH; ch++) v += acc[rt][h][ch];
                 if (HALF) v += __shfl_xor(v, 8, 64);     // the other block of the pair
-                part[((size_t)(wave * RT + rt) * 2 + h) * 64 + lane] = v;
+                part[((size_t)(wave * RT + rt) * NG + h) * 64 + lane] = v;
             }
         lds_barrier();
         if (wave < RT && have && (!HALF || kh == 0 || EPI == EPI_SWIGLU)) {
             const int rt = wave;
-            double y[2];
+            double y[NG];
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
+            for (int h = 0; h < NG; h++) {
                 double s = 0.0;
 #pragma unroll 4
-                for (int w2 = 0; w2 < kW; w2++) s += part[((size_t)(w2 * RT + rt) * 2 + h) * 64 + lane];
+                for (int w2 = 0; w2 < kW; w2++) s += part[((size_t)(w2 * RT + rt) * NG + h) * 64 + lane];
                 y[h] = s;
             }
             const int row = (grp_idx * RT + rt) * TR + (HALF ? 4 * (bq & 1) : 4 * bq) + kg;
             if (EPI == EPI_SWIGLU) {
                 // rows 2m (gate, even kg) and 2m + 1 (up, lane ^ 16)
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
+                for (int h = 0; h < NG; h++) {
                     const double yu = __shfl_xor(y[h], 16, 64);
                     const int c = e + 4 * h;
                     if (!(kg & 1) && kh == 0 && c < p.ncols && row + 1 < N) {
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
                 }
             } else if (row < N) {
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
+                for (int h = 0; h < NG; h++) {
                     const int c = e + 4 * h;
                     if (c >= p.ncols) continue;
                     const size_t col = (size_t)(p.col0 + c);
@@ -613,15 +614,21 @@ __global__ __launch_bounds__(gemm16_waves(RT, STAGED) * 64, (RT == 1 && STAGED) 
     }
 
     if (EPI == EPI_LOGITS) {
-        // per-lane bests belong to columns e and e + 4
-        float bv[8];
-        int bi[8];
+        // per-lane bests belong to columns e, e + 4, ...
+        float bv[4 * NG];
+        int bi[4 * NG];
 #pragma unroll
-        for (int c = 0; c < 8; c++) {
-            bv[c] = (c == e) ? best_v[0] : (c == e + 4) ? best_v[1] : -INFINITY;
-            bi[c] = (c == e) ? best_i[0] : (c == e + 4) ? best_i[1] : 0x7fffffff;
+        for (int c = 0; c < 4 * NG; c++) {
+            bv[c] = -INFINITY;
+            bi[c] = 0x7fffffff;
+#pragma unroll
+            for (int h = 0; h < NG; h++)
+                if (c == e + 4 * h) {
+                    bv[c] = best_v[h];
+                    bi[c] = best_i[h];
+                }
         }
-        argmax_tail<8>(p, bv, bi, bval, bidx, is_last, lane, wave, kW);
+        argmax_tail<4 * NG>(p, bv, bi, bval, bidx, is_last, lane, wave, kW);
     }
 }
 
@@ -664,8 +671,18 @@ size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round)
 // workgroup size of k_gemm16 with rt row tiles (staged: RMSNorm inputs)
 int mak_gemm16_threads(int rt, bool staged) { return gemm16_waves(rt, staged) * 64; }
 
-const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half)
+const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half, int ng)
 {
+    if (ng == 4) {   // 9..16 columns: one tile of 8 rows, raw inputs
+        if (rt != 1 || staged || !half) return nullptr;
+        switch (epi) {
+        case EPI_STORE: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_STORE, false, true, 4>);
+        case EPI_RESIDUAL: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_RESIDUAL, false, true, 4>);
+        case EPI_SWIGLU: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_SWIGLU, false, true, 4>);
+        case EPI_LOGITS: return reinterpret_cast<const void*>(&k_gemm8<1, EPI_LOGITS, false, true, 4>);
+        }
+        return nullptr;
+    }
     if (half) {   // one tile of 8 rows, raw inputs
         if (rt != 1 || staged) return nullptr;
         switch (epi) {
@@ -696,9 +713,9 @@ const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half)
 
 // dynamic LDS of a k_gemm8 launch (single_round: the partial tiles reuse the
 // staged inputs' space)
-size_t mak_gemm8_lds(int rt, int k, bool staged, bool single_round)
+size_t mak_gemm8_lds(int rt, int k, bool staged, bool single_round, int ng)
 {
-    if (!staged) return gemm8_part_lds(rt, false);
-    return single_round ? std::max(gemm16_input_lds(k), gemm8_part_lds(rt, true))
-                        : gemm16_input_lds(k) + gemm8_part_lds(rt, true);
+    if (!staged) return gemm8_part_lds(rt, false, ng);
+    return single_round ? std::max(gemm16_input_lds(k), gemm8_part_lds(rt, true, ng))
+                        : gemm16_input_lds(k) + gemm8_part_lds(rt, true, ng);
 }

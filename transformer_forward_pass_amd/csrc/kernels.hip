@@ -362,8 +362,8 @@ static const void* gemv_fn_r1(int epi)
 
 // gemm16.hip: the multi-column GEMM on the fp64 matrix cores
 const void* mak_gemm16_fn(int rt, int epi, bool staged);
-const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half);
-size_t mak_gemm8_lds(int rt, int k, bool staged, bool single_round);
+const void* mak_gemm8_fn(int rt, int epi, bool staged, bool half, int ng);
+size_t mak_gemm8_lds(int rt, int k, bool staged, bool single_round, int ng);
 size_t mak_gemm16_lds(int rt, int k, bool staged, bool single_round);
 int mak_gemm16_threads(int rt, bool staged);
 
@@ -420,7 +420,7 @@ static const void* gemv_fn(const GemvPhase& p)
         return mak_gemv4_fn(p.geo.r, mak_gemv_nc(p.ncols), p.epi);
     }
     if (p.multi == 2) return mak_gemm16_fn(p.rr, p.epi, p.in_kind != IN_RAW);
-    if (p.multi == 3) return mak_gemm8_fn(p.rr, p.epi, p.in_kind != IN_RAW, p.jw == 2);
+    if (p.multi == 3) return mak_gemm8_fn(p.rr, p.epi, p.in_kind != IN_RAW, p.jw == 2, p.ncols > 8 ? 4 : 2);
     if (p.multi) return gemvn_fn(p.rr, mak_gemv_nc(p.ncols), p.epi);
     if (const void* f = gemv1_fn(p)) return f;
     switch (p.geo.r) {
@@ -440,7 +440,8 @@ size_t mak_gemv_lds(const GemvPhase& p)
         const int tr = (p.multi == 3 && p.jw == 2) ? 8 : 16;   // rows per tile (k_gemm8 half-height: jw = 2)
         const int64_t groups = (p.geo.n_rows + tr * p.rr - 1) / (tr * p.rr);
         return p.multi == 2 ? mak_gemm16_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks)
-                            : mak_gemm8_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks);
+                            : mak_gemm8_lds(p.rr, p.geo.k, p.in_kind != IN_RAW, groups <= p.n_blocks,
+                                            p.ncols > 8 ? 4 : 2);
     }
     if (p.multi)
         return gemvn_lds(mak_gemv_nc(p.ncols), p.geo.k, p.rr, p.jw, p.geo.lr_log2, p.epi == EPI_SWIGLU);
@@ -650,7 +651,9 @@ int mak_gemm16_plan(const GemvPhase& p, int ncols, size_t lds_budget)
 // CUs idle).  Row tiles per workgroup as for k_gemm16, raw inputs at most
 // two.  Raw inputs whose 16-row groups are fewer than the CUs take tiles of
 // 8 rows (gemm8_half; MAK_GEMM8_HALF=0 turns them off), and with them any
-// K.  Returns 0 if the kernel does not apply.
+// K; on such tiles 9..16 columns run here too, as four groups of four
+// (MAK_GEMM8_WIDE=0 leaves them to k_gemm16).  Returns 0 if the kernel does
+// not apply.
 static bool gemm8_half(const GemvPhase& p)
 {
     static int hv = -1;
@@ -663,23 +666,27 @@ static bool gemm8_half(const GemvPhase& p)
 
 int mak_gemm8_plan(const GemvPhase& p, int ncols, size_t lds_budget)
 {
-    static int mc = -1;
+    static int mc = -1, wide = -1;
     if (mc < 0) {
         const char* e = getenv("MAK_GEMM8_COLS");
         mc = (e && atoi(e) >= 0) ? atoi(e) : 2;
+        const char* e2 = getenv("MAK_GEMM8_WIDE");
+        wide = (e2 && atoi(e2) == 0) ? 0 : 1;
     }
-    if (mc == 0 || ncols < mc || ncols < 2 || ncols > 8) return 0;
     const bool staged = p.in_kind != IN_RAW;
-    if (staged && p.geo.k > 4096) return 0;
     const bool half = gemm8_half(p);
+    if (mc == 0 || ncols < mc || ncols < 2 || ncols > 16) return 0;
+    if (ncols > 8 && !(wide && half)) return 0;
+    if (staged && p.geo.k > 4096) return 0;
     if (p.geo.k < 2048 || p.geo.n_rows < 2048 || (!staged && p.geo.k > 2048 && !half)) return 0;
     const int n_cu = device_cus();
     const int n16 = (p.geo.n_rows + 15) / 16;
     int rt = (n16 >= 8 * n_cu) ? 4 : (n16 >= 4 * n_cu) ? 2 : 1;
     if (!staged && rt > 2) rt = 2;
     if (half) rt = 1;
-    while (rt > 1 && mak_gemm8_lds(rt, p.geo.k, staged, false) > lds_budget) rt >>= 1;
-    return mak_gemm8_lds(rt, p.geo.k, staged, false) <= lds_budget ? rt : 0;
+    const int ng = ncols > 8 ? 4 : 2;
+    while (rt > 1 && mak_gemm8_lds(rt, p.geo.k, staged, false, ng) > lds_budget) rt >>= 1;
+    return mak_gemm8_lds(rt, p.geo.k, staged, false, ng) <= lds_budget ? rt : 0;
 }
 
 int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
@@ -711,8 +718,9 @@ int mak_gemv_blocks(GemvPhase& p, int cap, size_t lds_budget_n)
             p.threads = mak_gemm16_threads(rt, staged);
             const int tr = half ? 8 : 16;
             const int64_t groups = (p.geo.n_rows + tr * rt - 1) / (tr * rt);
-            const int occ = resident_blocks(mak_gemm8_fn(rt, p.epi, staged, half), p.threads,
-                                            mak_gemm8_lds(rt, p.geo.k, staged, false));
+            const int ng = p.ncols > 8 ? 4 : 2;
+            const int occ = resident_blocks(mak_gemm8_fn(rt, p.epi, staged, half, ng), p.threads,
+                                            mak_gemm8_lds(rt, p.geo.k, staged, false, ng));
             int64_t g = std::min<int64_t>(groups, (int64_t)occ * n_cu);
             if (p.epi == EPI_LOGITS) g = std::min<int64_t>(g, cap);
             return (int)std::max<int64_t>(1, g);
@@ -962,10 +970,11 @@ hipError_t mak_set_lds_limit(int bytes, int bytes_n, int attn_bytes)
                 hipError_t e = set(mak_gemm16_fn(rt, epi, staged), bytes_n);
                 if (e != hipSuccess) return e;
                 for (bool half : {false, true})
-                    if (const void* f8 = mak_gemm8_fn(rt, epi, staged, half)) {
-                        e = set(f8, bytes_n);
-                        if (e != hipSuccess) return e;
-                    }
+                    for (int ng : {2, 4})
+                        if (const void* f8 = mak_gemm8_fn(rt, epi, staged, half, ng)) {
+                            e = set(f8, bytes_n);
+                            if (e != hipSuccess) return e;
+                        }
             }
     for (int r : {1, 2, 4})
         for (int j : {1, 2, 3, 4, 6, 9, 11, 16})
