@@ -92,7 +92,8 @@ def _gemv_bytes(shape, kind):
 
 def _on_matrix_cores(shape, kind, ncols):
     """Whether the library's planner runs a multi-column GEMM of this kind on
-    the fp64 matrix cores: 9-16 columns always (k_gemm16); 2-8 columns where
+    the fp64 matrix cores: 9-16 columns always (k_gemm16, or k_gemm8 as four
+    column groups for raw inputs on few row groups); 2-8 columns where
     it picks k_gemm8 (at least 2048 inputs and 2048 rows, raw inputs -- O and
     down -- only at 2048 inputs)."""
     if ncols >= 9:
@@ -434,7 +435,7 @@ def measure_long_prefill(args, name="llama-3.2-1b-p2040", reps=2):
     return {"workload": "%s-shaped random-init decoder: %d-token prompt, chunks of 16" % (shape.name, P),
             "prefill_ms": round(res[16] * 1e3, 3), "prefill_tok_s": round(P / res[16], 1),
             "prefill_ms_chunk8": round(res[8] * 1e3, 3),
-            "mfma_roofline": {"bound": "mfma", "kernel": "weight GEMMs (k_gemm16)", "achieved": round(achieved, 2),
+            "mfma_roofline": {"bound": "mfma", "kernel": "weight GEMMs (k_gemm16, k_gemm8)", "achieved": round(achieved, 2),
                               "peak": FP64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s (fp64)",
                               "frac": round(achieved / FP64_MFMA_PEAK_TFLOPS, 4)},
             "phase_ms": {k: round(v[0], 3) for k, v in times.items()}}
