@@ -1,5 +1,9 @@
-// gemm16.hip -- the multi-column GEMM of batched decode and prefill chunks on
-// gfx950's fp64 matrix cores: y[c] = W x[c] for up to 16 columns.
+// gemm16.hip -- the multi-column GEMMs of batched decode and prefill chunks on
+// gfx950's fp64 matrix cores: y[c] = W x[c] for up to 16 columns.  k_gemm16
+// (v_mfma_f64_16x16x4_f64) serves 9..16 columns; k_gemm8
+// (v_mfma_f64_4x4x4_4b_f64, four independent 4x4 tiles per instruction)
+// serves 2..8 columns with no padded half tile, and 9..16 columns of raw
+// inputs on half-height tiles.  Both share the input staging.
 //
 // Every dot product of the decode path is exact in fp64 before its single
 // rounding (bf16 x bf16 products are exact in fp64), so a column computed
