@@ -1,14 +1,16 @@
 """Steps of 2..8 columns on the fp64 matrix cores (v_mfma_f64_4x4x4_4b_f64,
 k_gemm8), which the planner picks for GEMMs of at least 2048 inputs and
 2048 rows, with tiles of 8 rows for raw inputs whose 16-row groups would be
-fewer than the CUs.  Two one-layer shapes inside that region run every
+fewer than the CUs.  Three one-layer shapes inside that region run every
 epilogue through it: QKV (RMSNorm inputs, store), O (raw inputs, residual),
 gate/up (RMSNorm inputs, SwiGLU), down (raw inputs, residual) and the LM
 head (RMSNorm inputs, logits and greedy argmax); O and down on 8-row tiles,
 the rest on 16-row tiles (the second shape: a 3072-row gate/up and a
 6144-row LM head; its 1536-input down stays on the vector units).  With 11
 and 16 sequences O and down run as four groups of four columns on
-half-height tiles, the rest on the 16x16 instruction (k_gemm16).  Batched
+half-height tiles, the rest on the 16x16 instruction (k_gemm16).  The third
+shape takes workgroups of 2 and 4 row tiles (its gate/up and LM head) and a
+down projection of 8192 inputs on half-height tiles.  Batched
 decode must equal decoding each sequence alone (the one-column kernels)
 bitwise, a chunked prompt must equal token-by-token consumption bitwise, and
 both must match the CPU oracle ("model-as-a-kernel", API: decode_batch and chunked
@@ -26,6 +28,10 @@ SHAPES = {
                                intermediate=2048, vocab=2048, max_batch=16),
     "i1536": synth.small_shape(n_layers=1, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
                                intermediate=1536, vocab=6144, max_batch=16),
+    # workgroups of 2 row tiles (a 16384-row gate/up) and 4 (a 33000-row LM
+    # head), and a down projection of 8192 inputs on half-height tiles
+    "i8192": synth.small_shape(n_layers=1, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                               intermediate=8192, vocab=33000, max_batch=16),
 }
 STEPS = 3
 
