@@ -334,7 +334,7 @@ def measure_batched(args, name="tinyllama-1.1b", reps=2):
 
 def measure_long(args, name="qwen3-0.6b", reps=2):
     """Long context: a 512-token prompt in 64 chunks of 8 (the workload's
-    chunk), then 256 greedy tokens (attention runs split-KV past 384
+    chunk), then 256 greedy tokens (decode attention runs split-KV past 384
     positions at head_dim 128)."""
     import torch
     from transformer_forward_pass_amd import mak, synth
@@ -396,7 +396,7 @@ FP64_MFMA_PEAK_TFLOPS = 78.6
 
 def measure_long_prefill(args, name="llama-3.2-1b-p2040", reps=2):
     """Long-prompt prefill: a 2040-token prompt on the 1B shape in chunks of
-    16 (the GEMMs on the fp64 matrix cores; attention split-KV past 768
+    16 (the GEMMs on the fp64 matrix cores; single-pass attention up to 2048
     positions), and in chunks of 8 for comparison.  Reports the prompt's
     prefill time and the fp64 rate of its weight GEMMs (2 flops per weight
     per token) against the fp64 matrix peak."""

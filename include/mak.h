@@ -202,11 +202,12 @@ int mak_set_executor(mak_model *m, int executor);
 /* Attention work split ("model-as-a-kernel", Method section: split-KV with
  * a deterministic combine).  While a step's largest context pos + 1 is at
  * most `above` (default 49152 / head_dim: 384 at head_dim 128, 768 at 64,
- * where the split form starts to pay), each query head's attention runs in one
- * workgroup over all positions; beyond it, or past the single-pass capacity
- * of 4096 positions, attention runs split-KV: scores and a maximum per chunk
- * of 128 positions, then the exact global softmax and P.V per chunk, then
- * the chunk sums in chunk order.  Both forms give bitwise-identical results;
+ * where the split form starts to pay; for prompt chunks 131072 / head_dim,
+ * where their blockwise form does; a call sets both to `above`), each query
+ * head's attention runs in one workgroup over all positions; beyond it, or
+ * past the single-pass capacity of 4096 positions, attention runs split-KV:
+ * scores and a maximum per chunk of 128 positions, then the exact global
+ * softmax and P.V per chunk, then the chunk sums in chunk order.  Both forms give bitwise-identical results;
  * 0 always splits.  Returns MAK_EINVAL for a negative threshold. */
 int mak_set_attention_split(mak_model *m, int32_t above);
 

@@ -12,7 +12,8 @@ and the oracle's 16 largest logits.  Each benchmark configuration is covered
 at its own size: batch-1 decode of the 135M, 1B and Qwen3 shapes, Qwen3's
 512-token prompt in chunks of 16, TinyLlama batches of 8 and 16 sequences,
 a 2040-token prompt on the 1B shape in chunks of 16 (long-prompt
-prefill; split-KV attention past 768 positions), and the 1B shape with 4-bit
+prefill: single-pass attention, and blockwise split-KV past 768 positions
+bitwise equal to it), and the 1B shape with 4-bit
 (MXFP4) per-layer weights, against the oracle run on the dequantized
 weights."""
 import json
@@ -167,9 +168,11 @@ def test_full_workload_batched16_tinyllama():
 
 def test_long_prompt_prefill_1b():
     """A 2040-token prompt on the 1B shape consumed 16 tokens per step (the
-    GEMMs on the fp64 matrix cores, attention split-KV past 768 positions):
-    the prompt's last-token logits and two teacher-forced decode steps over
-    [V], and the free-running stream."""
+    GEMMs on the fp64 matrix cores; attention single-pass, the default for
+    prompt chunks of this length): the prompt's last-token logits and two
+    teacher-forced decode steps over [V], and the free-running stream.  The
+    same prompt with blockwise split-KV attention past 768 positions gives
+    bitwise the same logits and KV cache."""
     name = "llama-3.2-1b-p2040"
     g, full, wl, m = _load(name)
     seq = g["sequences"][0]
@@ -178,4 +181,11 @@ def test_long_prompt_prefill_1b():
     got = m.generate(seq["prompt"], wl.max_new)
     tokens_ok(got, seq["tokens"], seq["gaps"], name)
     _teacher_forced(m, g, full, name, chunk=16)
+    single = m.prefill(seq["prompt"]).double().cpu().numpy()
+    k1, v1 = m.read_kv(7, 0, 0, 2040)
+    m.set_attention_split(768)
+    block = m.prefill(seq["prompt"]).double().cpu().numpy()
+    k2, v2 = m.read_kv(7, 0, 0, 2040)
+    assert np.array_equal(single, block), "blockwise != single-pass prompt logits"
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2), "blockwise != single-pass KV"
     m.free()

@@ -87,6 +87,11 @@ constexpr int kAttnSinglePassMax = 4096;   // most positions of the single-pass 
 // about where the three split launches overtake the single pass (measured:
 // ~300 positions at head_dim 128, ~750 at 64)
 constexpr int kAttnSplitWork = 48 * 1024;
+// prompt chunks (the consecutive positions of one sequence) stay single-pass
+// longer: 128K / head_dim positions (measured: a 2040-token prompt in chunks
+// of 16 at head_dim 64 takes 213 ms with the decode threshold, 202 ms all
+// single-pass; a 512-token prompt in chunks of 8 at head_dim 128 95 -> 88 ms)
+constexpr int kAttnPromptSplitWork = 128 * 1024;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -474,6 +479,7 @@ struct mak_model {
     bool use_graphs = true;
     int prefill_chunk = MAK_PREFILL_CHUNK;   // prompt tokens per prefill step (<= MAK_MAX_COLS)
     int split_above = 0;                 // split-KV attention once pos + 1 exceeds this
+    int prompt_split_above = 0;          // the same for prompt chunks (blockwise)
     bool block_attn = true;              // prompt chunks past split_above run blockwise
     std::vector<StepGraph> graphs;
     Layout L;
@@ -774,7 +780,8 @@ StepScratch arena_scratch(const mak_model* m)
 // blockwise for a prompt chunk of two or more columns.
 int attn_mode(const mak_model* m, int max_n, int ncols = 1, bool one_seq = false)
 {
-    if (max_n <= m->split_above && max_n <= m->L.s_cap) return ATTN_SINGLE;
+    const int above = (one_seq && ncols >= 2) ? m->prompt_split_above : m->split_above;
+    if (max_n <= above && max_n <= m->L.s_cap) return ATTN_SINGLE;
     return (one_seq && ncols >= 2 && m->block_attn) ? ATTN_BLOCK : ATTN_SPLIT;
 }
 
@@ -1060,6 +1067,7 @@ int mak_load(const mak_config* cfg, const mak_weights* w, void* d_arena, size_t 
     m->stream = st;
     m->slot_len.assign(c.max_batch, 0);
     m->split_above = kAttnSplitWork / c.head_dim;
+    m->prompt_split_above = kAttnPromptSplitWork / c.head_dim;
     m->cur = st;
     if (hipStreamCreateWithFlags(&m->capture, hipStreamNonBlocking) != hipSuccess) {
         delete m;
@@ -1120,6 +1128,7 @@ int mak_set_attention_split(mak_model* m, int32_t above)
     if (rc) return rc;
     if (above < 0) return fail(MAK_EINVAL, "split threshold %d < 0", above);
     m->split_above = above;
+    m->prompt_split_above = above;
     return MAK_OK;
 }
 
